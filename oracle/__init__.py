@@ -1,0 +1,40 @@
+"""fp64 CPU oracle for the joint text+image DiT attention step.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check in
+``__graft_entry__`` and the CPU-baseline leg of ``bench.py`` may import or run
+anything in this package.  The product path (the C-ABI library and its Python
+binding) never calls it, and this package imports nothing from the product
+path: the two share no kernels, helpers, tables or constants.  The only code
+both sides use is the seeded input generator in ``workloads``, which holds none
+of the method's arithmetic.
+
+What it computes, each step written from its definition on the pages, in
+float64 NumPy, slow and plain:
+
+* ``metadata.build_token_metadata`` -- per-token image-block ids (text = -1),
+  target-image mask, rotary positions and the exclusive key bound of each
+  query (QwenImage21Transformer2DModel API page, ``build_token_metadata``).
+* ``qknorm_rope.rms_norm`` / ``qknorm_rope.rope`` -- per-head RMSNorm of Q and
+  K, then rotary embedding over the (frame, height, width) axes or the
+  Lumina 2D split (NucleusMoE-Image pipeline article, section 6.3; Lumina-Next
+  DiT article, configuration table and section 4).
+* ``attention.attention`` -- softmax attention under the full mask or the
+  block-causal rule "q_idx >= kv_idx or same image block", with GQA and an
+  optional cached K/V prefix (QwenImage21Transformer2DModel API page, the
+  block-causal and causal_condition notes and ``forward``'s kv_cache modes).
+* ``attention.attention_multipass`` -- the same masked attention computed
+  segment by segment (one pass per text run or image block), the second,
+  independent implementation of the mask that the page says gives the same
+  result.
+* ``attention.attention_bruteforce`` -- quadruple Python loops, tiny inputs.
+
+Pins: every function is pinned by tests under ``tests/`` that do not re-type
+its formula: closed forms, invariants (rotation preserves norms, relative
+phase), textbook special cases checked against library routines
+(``torch.nn.functional.scaled_dot_product_attention`` in float64 on the CPU),
+single-pass == multi-pass, cached rows == full rows, brute force on tiny
+inputs, and hand-derived token-metadata fixtures under ``tests/golden``.
+The pages print no numeric worked example for this step, so no pin is a
+printed value; none of the functions is left unpinned.
+"""
+from . import metadata, qknorm_rope, attention, pipeline  # noqa: F401

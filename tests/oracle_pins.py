@@ -1,0 +1,330 @@
+"""Pins of the fp64 oracle against facts fixed by the pages or by mathematics.
+
+Each pin is a plain function that raises AssertionError when the oracle
+disagrees.  ``test_oracle_*.py`` run them; ``test_oracle_mutations.py`` plants
+plausible mistakes in the oracle and checks that some pin catches each one.
+None of these re-types the oracle's own formula: they use hand-derived
+fixtures, closed forms, invariants, library routines (torch SDPA in float64 on
+the CPU, torch.repeat_interleave) and brute force.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+import oracle.attention as att
+import oracle.metadata as meta
+import oracle.qknorm_rope as qr
+from tests import goldens
+from workloads import Workload, sequence_inputs, small_workload
+
+
+# --------------------------------------------------------------------------- helpers
+def _layout_inputs(layout):
+    w = small_workload("fixture", 1, 1, 1, 8, layout, (8,))
+    return sequence_inputs(w)
+
+
+def _sdpa(q, k, v, is_causal=False):
+    """torch SDPA in float64 on the CPU; inputs BSHD numpy, output BSHD numpy."""
+    tq = torch.from_numpy(np.ascontiguousarray(q.transpose(0, 2, 1, 3)))
+    tk = torch.from_numpy(np.ascontiguousarray(k.transpose(0, 2, 1, 3)))
+    tv = torch.from_numpy(np.ascontiguousarray(v.transpose(0, 2, 1, 3)))
+    o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=is_causal)
+    return o.numpy().transpose(0, 2, 1, 3)
+
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+# --------------------------------------------------------------------------- metadata
+def pin_metadata_goldens():
+    """Hand-derived fixtures (tests/golden/metadata_*.txt), each citing its rule."""
+    for name in goldens.metadata_fixtures():
+        g = goldens.load(name)
+        mask, shapes = _layout_inputs(g["layout"])
+        md = meta.build_token_metadata(mask, shapes, g["pos_mode"])
+        for key in ("image_ids", "target_mask", "kv_limit", "pos_ids"):
+            assert np.array_equal(md[key].astype(np.int64), g[key]), (name, key, md[key], g[key])
+
+
+def random_layout(rng, max_tokens=60):
+    segs = []
+    n = 0
+    while n < max_tokens:
+        if rng.random() < 0.5:
+            t = int(rng.integers(1, 6))
+            segs.append(("T", t))
+            n += t
+        else:
+            f, h, w = int(rng.integers(1, 3)), 2 * int(rng.integers(1, 3)), 2 * int(rng.integers(1, 3))
+            segs.append(("I", f, h, w))
+            n += f * h * w
+    return tuple(segs)
+
+
+def pin_kv_limit_is_predicate_prefix(trials=40):
+    """For every query, the set of keys the literal block-causal predicate allows
+    (brute force over all pairs, straight from the page's rule) is exactly the
+    prefix [0, kv_limit[q]); kv_limit never decreases along the sequence."""
+    rng = np.random.default_rng(11)
+    for _ in range(trials):
+        layout = random_layout(rng)
+        mask, shapes = _layout_inputs(layout)
+        md = meta.build_token_metadata(mask, shapes)
+        ids = md["image_ids"]
+        S = len(ids)
+        for qi in range(S):
+            allowed = [kj for kj in range(S) if kj <= qi or (ids[qi] >= 0 and ids[qi] == ids[kj])]
+            assert allowed == list(range(md["kv_limit"][qi])), (layout, qi)
+        assert np.all(np.diff(md["kv_limit"]) >= 0)
+
+
+def pin_metadata_errors():
+    """Readings for inputs the pages leave undefined raise errors."""
+    def expect_error(mask, shapes, mode="centered_fhw"):
+        try:
+            meta.build_token_metadata(mask, shapes, mode)
+        except meta.MetadataError:
+            return
+        raise AssertionError("no error for %r %r" % (mask, shapes))
+    expect_error([1, 1, 1], [(1, 2, 2)])                 # count mismatch
+    expect_error([1, 1, 0, 1, 1], [(1, 2, 2)])           # block split by text
+    expect_error([1] * 6, [(1, 3, 2)])                   # odd height, centred
+    expect_error([0, 1, 1], [(1, 1, 2)], "grid_hw")      # text in 2D mode
+    expect_error([1] * 8, [(2, 2, 2)], "grid_hw")        # multi-frame in 2D mode
+
+
+# --------------------------------------------------------------------------- rmsnorm
+def pin_rmsnorm_closed_forms():
+    # x = (3, 4), eps = 0: mean square 12.5, so y = x * sqrt(2) / 5.
+    y = qr.rms_norm(np.array([3.0, 4.0]), np.ones(2), 0.0)
+    assert np.allclose(y, [3 * math.sqrt(2) / 5, 4 * math.sqrt(2) / 5], rtol=0, atol=1e-15)
+    # With unit weights mean(y^2) = m / (m + eps), m = mean(x^2); use a large eps
+    # so that any other placement of eps shows.
+    x = _rand((3, 5, 4, 16), 1)
+    for eps in (0.0, 0.5, 3.0):
+        y = qr.rms_norm(x, np.ones(16), eps)
+        m = np.mean(x * x, axis=-1)
+        assert np.allclose(np.mean(y * y, axis=-1), m / (m + eps), rtol=1e-12, atol=0)
+    # The weight multiplies channel by channel.
+    wv = 1.0 + 0.1 * _rand((16,), 2)
+    assert np.allclose(qr.rms_norm(x, wv, 1e-6), qr.rms_norm(x, np.ones(16), 1e-6) * wv, rtol=1e-13)
+    # Each head is normalised on its own: changing head 0 leaves head 1.
+    x2 = x.copy()
+    x2[:, :, 0, :] *= 7.0
+    assert np.array_equal(qr.rms_norm(x2, wv, 1e-6)[:, :, 1:], qr.rms_norm(x, wv, 1e-6)[:, :, 1:])
+
+
+# --------------------------------------------------------------------------- rope
+def pin_rope_rotation():
+    axes = (16, 56, 56)
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((2, 7, 3, 128))
+    pos = rng.integers(-40, 1100, size=(7, 3))
+    y = qr.rope(x, pos, axes)
+    # A rotation keeps every channel pair's length, hence each head's norm.
+    pairs_x = np.hypot(x[..., 0::2], x[..., 1::2])
+    pairs_y = np.hypot(y[..., 0::2], y[..., 1::2])
+    assert np.allclose(pairs_x, pairs_y, rtol=1e-12)
+    # Position 0 is the identity.
+    assert np.allclose(qr.rope(x, np.zeros((7, 3), int), axes), x, rtol=0, atol=0)
+
+
+def pin_rope_pairing_and_ladder():
+    """Adjacent pairs (2j, 2j+1); the first pair of each axis turns by exactly the
+    position in radians; closed-form ladder points theta^(-2j/d):
+    d = 16, j = 2 -> 0.1 and j = 4 -> 0.01; d = 4 (Lumina mini 4+4), j = 1 -> 0.01."""
+    def turn(axes, axis, pair, p):
+        D = sum(axes)
+        off = sum(axes[:axis])
+        x = np.zeros((1, 1, 1, D))
+        x[..., off + 2 * pair] = 1.0
+        pos = np.zeros((1, 3), int)
+        pos[0, axis] = p
+        y = qr.rope(x, pos, axes)[0, 0, 0]
+        nz = np.flatnonzero(np.abs(y) > 1e-300)
+        assert set(nz) <= {off + 2 * pair, off + 2 * pair + 1}, (axes, axis, pair, nz)
+        return y[off + 2 * pair], y[off + 2 * pair + 1]
+    for axes in ((16, 56, 56), (36, 36), (4, 4), (8, 4, 4)):
+        for a in range(len(axes)):
+            c, s = turn(axes, a, 0, 5)
+            assert abs(c - math.cos(5)) < 1e-15 and abs(s - math.sin(5)) < 1e-15
+    for (axes, a, j, omega) in (((16, 56, 56), 0, 2, 0.1), ((16, 56, 56), 0, 4, 0.01), ((4, 4), 1, 1, 0.01)):
+        p = 300
+        c, s = turn(axes, a, j, p)
+        assert abs(c - math.cos(p * omega)) < 1e-12 and abs(s - math.sin(p * omega)) < 1e-12, (axes, j)
+    # A position on one axis moves only that axis's channels.
+    x = _rand((1, 1, 1, 128), 4)
+    pos = np.array([[0, 9, 0]])
+    y = qr.rope(x, pos, (16, 56, 56))
+    assert np.array_equal(y[..., :16], x[..., :16]) and np.array_equal(y[..., 72:], x[..., 72:])
+    assert not np.allclose(y[..., 16:72], x[..., 16:72])
+
+
+def pin_rope_relative():
+    """q.k after rotation depends on the positions only through their difference."""
+    axes = (16, 56, 56)
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((1, 1, 1, 128))
+    k = rng.standard_normal((1, 1, 1, 128))
+    for _ in range(20):
+        pq = rng.integers(-64, 1100, size=(1, 3))
+        pk = rng.integers(-64, 1100, size=(1, 3))
+        shift = rng.integers(-500, 500, size=(1, 3))
+        d0 = np.sum(qr.rope(q, pq, axes) * qr.rope(k, pk, axes))
+        d1 = np.sum(qr.rope(q, pq + shift, axes) * qr.rope(k, pk + shift, axes))
+        assert abs(d0 - d1) < 1e-9 * (1 + abs(d0))
+
+
+# --------------------------------------------------------------------------- attention
+def pin_full_is_sdpa():
+    """One image block and no text: the full mask and the block-causal mask both
+    equal plain bidirectional attention (torch SDPA, float64, CPU)."""
+    rng = np.random.default_rng(6)
+    q, k, v = (rng.standard_normal((2, 24, 4, 16)) for _ in range(3))
+    ids = np.zeros(24, int)
+    ref = _sdpa(q, k, v)
+    for mode in ("full", "block_causal"):
+        o, _ = att.attention(q, k, v, ids, mode)
+        assert np.allclose(o, ref, rtol=1e-10, atol=1e-12), mode
+
+
+def pin_text_only_is_causal():
+    """No image block: block-causal equals plain causal attention."""
+    rng = np.random.default_rng(7)
+    q, k, v = (rng.standard_normal((2, 20, 3, 8)) for _ in range(3))
+    ids = -np.ones(20, int)
+    o, _ = att.attention(q, k, v, ids, "block_causal")
+    assert np.allclose(o, _sdpa(q, k, v, is_causal=True), rtol=1e-10, atol=1e-12)
+    o2, _ = att.attention_multipass(q, k, v, ids)
+    assert np.allclose(o2, o, rtol=1e-10, atol=1e-12)
+
+
+def pin_gqa_is_repeat_interleave():
+    """GQA equals multi-head attention over K/V heads expanded by
+    repeat_interleave (each KV head serves a contiguous group of query heads)."""
+    rng = np.random.default_rng(8)
+    q = rng.standard_normal((1, 12, 6, 8))
+    k, v = (rng.standard_normal((1, 12, 2, 8)) for _ in range(2))
+    ids = np.zeros(12, int)
+    o, _ = att.attention(q, k, v, ids, "full")
+    ke = torch.repeat_interleave(torch.from_numpy(k), 3, dim=2).numpy()
+    ve = torch.repeat_interleave(torch.from_numpy(v), 3, dim=2).numpy()
+    assert np.allclose(o, _sdpa(q, ke, ve), rtol=1e-10, atol=1e-12)
+
+
+def pin_singlepass_equals_multipass(trials=12):
+    """The one-pass masked result equals the per-prefix-segment multi-pass result
+    (the page states both processors give the same output)."""
+    rng = np.random.default_rng(9)
+    layouts = [(("T", 16), ("I", 1, 4, 4)),
+               (("T", 8), ("I", 1, 4, 4), ("I", 1, 2, 4), ("T", 6), ("I", 1, 4, 4)),
+               (("I", 1, 2, 2), ("I", 1, 2, 2))]
+    layouts += [random_layout(rng, 50) for _ in range(trials)]
+    for layout in layouts:
+        mask, shapes = _layout_inputs(layout)
+        ids = meta.build_token_metadata(mask, shapes)["image_ids"]
+        S = len(ids)
+        q = rng.standard_normal((1, S, 4, 8))
+        k, v = (rng.standard_normal((1, S, 2, 8)) for _ in range(2))
+        o1, l1 = att.attention(q, k, v, ids, "block_causal")
+        o2, l2 = att.attention_multipass(q, k, v, ids)
+        assert np.allclose(o1, o2, rtol=1e-10, atol=1e-12), layout
+        assert np.allclose(l1, l2, rtol=1e-10, atol=1e-12), layout
+
+
+def pin_adjacent_blocks_stay_separate():
+    """Rows of the first of two adjacent condition blocks do not see the second
+    block's keys; the second block sees the first (it comes earlier)."""
+    mask, shapes = _layout_inputs((("T", 3), ("I", 1, 2, 2), ("I", 1, 2, 2), ("I", 1, 2, 2)))
+    ids = meta.build_token_metadata(mask, shapes)["image_ids"]
+    rng = np.random.default_rng(10)
+    S = len(ids)
+    q, k, v = (rng.standard_normal((1, S, 2, 8)) for _ in range(3))
+    o, _ = att.attention(q, k, v, ids, "block_causal")
+    k2, v2 = k.copy(), v.copy()
+    k2[:, 7:11] += 1.0
+    v2[:, 7:11] += 1.0                      # perturb block 1 (positions 7..10)
+    o2, _ = att.attention(q, k2, v2, ids, "block_causal")
+    assert np.array_equal(o[:, :7], o2[:, :7])           # text and block 0 unaffected
+    assert not np.allclose(o[:, 7:], o2[:, 7:])
+
+
+def pin_cached_equals_full():
+    """Cached-prefix decode: the target rows computed from cached prefix K/V equal
+    the same rows of the full forward; the prefix rows do not depend on the
+    target's K/V."""
+    layout = (("T", 6), ("I", 1, 2, 2), ("I", 1, 2, 4))
+    mask, shapes = _layout_inputs(layout)
+    ids = meta.build_token_metadata(mask, shapes)["image_ids"]
+    S, P = len(ids), 10
+    rng = np.random.default_rng(12)
+    q = rng.standard_normal((2, S, 4, 8))
+    k, v = (rng.standard_normal((2, S, 2, 8)) for _ in range(2))
+    full, full_lse = att.attention(q, k, v, ids, "block_causal")
+    cached, cached_lse = att.attention(q[:, P:], k, v, ids, "block_causal", q_offset=P)
+    assert np.allclose(cached, full[:, P:], rtol=1e-12, atol=1e-14)
+    assert np.allclose(cached_lse, full_lse[:, :, P:], rtol=1e-12, atol=1e-14)
+    k2, v2 = k.copy(), v.copy()
+    k2[:, P:] = rng.standard_normal(k2[:, P:].shape)
+    v2[:, P:] = rng.standard_normal(v2[:, P:].shape)
+    full2, _ = att.attention(q, k2, v2, ids, "block_causal")
+    assert np.array_equal(full2[:, :P], full[:, :P])
+
+
+def _nested(a):
+    return a.tolist()
+
+
+def pin_bruteforce_tiny():
+    """The vectorised oracle equals explicit loops on the pages' tiny shapes:
+    the tiny fp32 layout (2 heads x 32, text 16 + 1x4x4), the Lumina mini test
+    (3 heads over 1 KV head, head_dim 8, 2D rope 4+4 on a 4x4 grid) and the
+    NucleusMoE dummy test's axes (8, 4, 4) (head_dim 16)."""
+    rng = np.random.default_rng(13)
+    cases = [((("T", 16), ("I", 1, 4, 4)), 2, 2, 32, (4, 14, 14), "centered_fhw", "block_causal"),
+             ((("I", 1, 4, 4),), 3, 1, 8, (4, 4), "grid_hw", "full"),
+             ((("T", 5), ("I", 1, 2, 4), ("T", 2), ("I", 1, 2, 2)), 2, 1, 16, (8, 4, 4), "centered_fhw",
+              "block_causal")]
+    for layout, H, Hk, D, axes, pos_mode, mode in cases:
+        mask, shapes = _layout_inputs(layout)
+        md = meta.build_token_metadata(mask, shapes, pos_mode)
+        S = len(mask)
+        q = qr.qknorm_rope(rng.standard_normal((1, S, H, D)), np.ones(D), 1e-6, md["pos_ids"], axes)
+        k = qr.qknorm_rope(rng.standard_normal((1, S, Hk, D)), np.ones(D), 1e-6, md["pos_ids"], axes)
+        v = rng.standard_normal((1, S, Hk, D))
+        o, lse = att.attention(q, k, v, md["image_ids"], mode)
+        ob, lb = att.attention_bruteforce(_nested(q), _nested(k), _nested(v), list(md["image_ids"]), mode)
+        assert np.allclose(o, np.asarray(ob), rtol=1e-11, atol=1e-13), layout
+        assert np.allclose(lse, np.asarray(lb), rtol=1e-11, atol=1e-13), layout
+
+
+def pin_lse_definition():
+    """lse is log sum_k exp(logit_k) over allowed keys: with V = identity-like
+    one-hot values the output row is exp(logit - lse) per key (torch.logsumexp
+    cross-check on a tiny block-causal case)."""
+    mask, shapes = _layout_inputs((("T", 3), ("I", 1, 2, 2)))
+    ids = meta.build_token_metadata(mask, shapes)["image_ids"]
+    S, D = 7, 8
+    rng = np.random.default_rng(14)
+    q, k = (rng.standard_normal((1, S, 1, D)) for _ in range(2))
+    v = np.zeros((1, S, 1, S))
+    v[0, :, 0, :] = np.eye(S)
+    o, lse = att.attention(q, k, v, ids, "block_causal")
+    logits = torch.from_numpy(q[0, :, 0] @ k[0, :, 0].T / math.sqrt(D))
+    allowed = torch.tensor([[j <= i or (ids[i] >= 0 and ids[i] == ids[j]) for j in range(S)] for i in range(S)])
+    ref_lse = torch.logsumexp(logits.masked_fill(~allowed, -math.inf), dim=1).numpy()
+    assert np.allclose(lse[0, 0], ref_lse, rtol=1e-12, atol=1e-13)
+    probs = torch.softmax(logits.masked_fill(~allowed, -math.inf), dim=1).numpy()
+    assert np.allclose(o[0, :, 0, :], probs, rtol=1e-12, atol=1e-14)
+
+
+ALL_PINS = [pin_metadata_goldens, pin_kv_limit_is_predicate_prefix, pin_metadata_errors,
+            pin_rmsnorm_closed_forms, pin_rope_rotation, pin_rope_pairing_and_ladder, pin_rope_relative,
+            pin_full_is_sdpa, pin_text_only_is_causal, pin_gqa_is_repeat_interleave,
+            pin_singlepass_equals_multipass, pin_adjacent_blocks_stay_separate, pin_cached_equals_full,
+            pin_bruteforce_tiny, pin_lse_definition]

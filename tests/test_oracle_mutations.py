@@ -1,0 +1,171 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that at least
+one pin catches each: evidence that the pins constrain the oracle."""
+import numpy as np
+import pytest
+
+import oracle.attention as att
+import oracle.metadata as meta
+import oracle.qknorm_rope as qr
+from tests import oracle_pins as pins
+
+
+def _fails(pin_list):
+    for pin in pin_list:
+        try:
+            pin()
+        except AssertionError:
+            return True
+    return False
+
+
+def _allowed_strict_causal(q_index, k_index, image_ids, mask_mode):
+    m = att.allowed_matrix.__wrapped__(q_index, k_index, image_ids, mask_mode)
+    return m & ~(np.asarray(k_index)[None, :] == np.asarray(q_index)[:, None]) | (
+        (np.asarray(image_ids)[np.asarray(q_index)][:, None] >= 0) & m)
+
+
+def _allowed_text_matches_text(q_index, k_index, image_ids, mask_mode):
+    if mask_mode == "full":
+        return np.ones((len(q_index), len(k_index)), bool)
+    ids = np.asarray(image_ids)
+    causal = np.asarray(k_index)[None, :] <= np.asarray(q_index)[:, None]
+    return causal | (ids[q_index][:, None] == ids[k_index][None, :])
+
+
+def _rms_sum(x, weight, eps):
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps) * weight
+
+
+def _rms_eps_outside(x, weight, eps):
+    x = np.asarray(x, dtype=np.float64)
+    return x / (np.sqrt(np.mean(x * x, axis=-1, keepdims=True)) + eps) * weight
+
+
+def _rope_rotate_half(x, pos, axes, theta=10000.0):
+    x = np.asarray(x, dtype=np.float64)
+    y = x.copy()
+    pos = np.asarray(pos, dtype=np.float64)
+    off = 0
+    for a, d_a in enumerate(axes):
+        half = d_a // 2
+        for j in range(half):
+            ph = pos[:, a] * theta ** (-2.0 * j / d_a)
+            c, s = np.cos(ph)[:, None], np.sin(ph)[:, None]
+            x0, x1 = x[..., off + j], x[..., off + j + half]
+            y[..., off + j] = x0 * c - x1 * s
+            y[..., off + j + half] = x0 * s + x1 * c
+        off += d_a
+    return y
+
+
+def _rope_shared_ladder(x, pos, axes, theta=10000.0):
+    """Mistake: one frequency ladder over the whole head instead of per axis."""
+    x = np.asarray(x, dtype=np.float64)
+    y = x.copy()
+    D = x.shape[-1]
+    pos = np.asarray(pos, dtype=np.float64)
+    off = 0
+    for a, d_a in enumerate(axes):
+        for j in range(d_a // 2):
+            ph = pos[:, a] * theta ** (-2.0 * (off // 2 + j) / D)
+            c, s = np.cos(ph)[:, None], np.sin(ph)[:, None]
+            x0, x1 = x[..., off + 2 * j], x[..., off + 2 * j + 1]
+            y[..., off + 2 * j] = x0 * c - x1 * s
+            y[..., off + 2 * j + 1] = x0 * s + x1 * c
+        off += d_a
+    return y
+
+
+def _rope_sign_flip(x, pos, axes, theta=10000.0):
+    return qr_rope_orig(x, -np.asarray(pos), axes, theta)
+
+
+qr_rope_orig = qr.rope
+att_attention_orig = att.attention
+
+
+def _attention_gqa_modulo(q, k, v, image_ids, mask_mode, scale=None, q_offset=0, rows=None, chunk=2048):
+    # Mistake: query head h reads KV head h % H_kv instead of h // G.
+    H, Hk = q.shape[2], k.shape[2]
+    perm = [h % Hk for h in range(H)]
+    ke = np.asarray(k)[:, :, perm]
+    ve = np.asarray(v)[:, :, perm]
+    return att_attention_orig(q, ke, ve, image_ids, mask_mode, scale, q_offset, rows, chunk)
+
+
+def _attention_no_scale(q, k, v, image_ids, mask_mode, scale=None, q_offset=0, rows=None, chunk=2048):
+    return att_attention_orig(q, k, v, image_ids, mask_mode, 1.0, q_offset, rows, chunk)
+
+
+def _metadata_merge_runs(image_pad_mask, img_shapes, pos_mode="centered_fhw"):
+    """Mistake: blocks taken from contiguous runs of True (merges adjacent images)."""
+    md = meta_build_orig(image_pad_mask, img_shapes, pos_mode)
+    ids = md["image_ids"].copy()
+    run, prev = -1, False
+    for s, m in enumerate(image_pad_mask):
+        if m and not prev:
+            run += 1
+        ids[s] = run if m else -1
+        prev = bool(m)
+    md["image_ids"] = ids
+    return md
+
+
+meta_build_orig = meta.build_token_metadata
+
+
+def _metadata_kv_limit_off_by_one(image_pad_mask, img_shapes, pos_mode="centered_fhw"):
+    md = meta_build_orig(image_pad_mask, img_shapes, pos_mode)
+    md["kv_limit"] = md["kv_limit"] - (md["image_ids"] >= 0)
+    return md
+
+
+def _metadata_uncentred(image_pad_mask, img_shapes, pos_mode="centered_fhw"):
+    md = meta_build_orig(image_pad_mask, img_shapes, pos_mode)
+    if pos_mode == "centered_fhw":
+        pos = md["pos_ids"].copy()
+        off = 0
+        for s, b in enumerate(md["image_ids"]):
+            if b >= 0:
+                f, h, w = img_shapes[b]
+                pos[s, 1] += h // 2
+                pos[s, 2] += w // 2
+        md["pos_ids"] = pos
+    return md
+
+
+def _wrap_allowed(fn):
+    orig = att.allowed_matrix
+
+    def wrapped(*a, **k):
+        return fn(*a, **k)
+    wrapped.__wrapped__ = orig
+    return wrapped
+
+
+MUTATIONS = [
+    ("block_causal_drops_diagonal", att, "allowed_matrix",
+     lambda q, k, ids, mode: (att.allowed_matrix.__wrapped__(q, k, ids, mode)
+                              & ~(np.asarray(k)[None, :] == np.asarray(q)[:, None])) if mode != "full"
+     else np.ones((len(q), len(k)), bool)),
+    ("text_ids_count_as_one_block", att, "allowed_matrix", _allowed_text_matches_text),
+    ("rmsnorm_sum_not_mean", qr, "rms_norm", _rms_sum),
+    ("rmsnorm_eps_outside_sqrt", qr, "rms_norm", _rms_eps_outside),
+    ("rope_rotate_half_pairs", qr, "rope", _rope_rotate_half),
+    ("rope_shared_frequency_ladder", qr, "rope", _rope_shared_ladder),
+    ("rope_negated_phase", qr, "rope", _rope_sign_flip),
+    ("gqa_modulo_head_map", att, "attention", _attention_gqa_modulo),
+    ("softmax_scale_missing", att, "attention", _attention_no_scale),
+    ("metadata_merges_adjacent_images", meta, "build_token_metadata", _metadata_merge_runs),
+    ("metadata_kv_limit_off_by_one", meta, "build_token_metadata", _metadata_kv_limit_off_by_one),
+    ("metadata_positions_uncentred", meta, "build_token_metadata", _metadata_uncentred),
+]
+
+
+@pytest.mark.parametrize("name,module,attr,fn", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_mutation_is_caught(monkeypatch, name, module, attr, fn):
+    if attr == "allowed_matrix":
+        fn = _wrap_allowed(fn)
+    monkeypatch.setattr(module, attr, fn)
+    assert _fails(pins.ALL_PINS), "no pin caught the planted mistake %s" % name

@@ -1,0 +1,9 @@
+"""The fp64 oracle against what the pages and mathematics fix (CPU only)."""
+import pytest
+
+from tests import oracle_pins
+
+
+@pytest.mark.parametrize("pin", oracle_pins.ALL_PINS, ids=lambda f: f.__name__)
+def test_pin(pin):
+    pin()
