@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Benchmark of the joint text+image DiT attention step on one MI355X.
+
+A step is one pass of the whole path on one batch of synthetic inputs that
+are already resident in HBM: token metadata -> fused QK-RMSNorm + rotary ->
+masked attention (the cached-prefix workload runs the cached attention entry
+point instead of the plain one).  Default workload: batch 2, 32 heads x 128,
+1024 text tokens followed by one 1x64x64 target image block (5120 tokens),
+block-causal mask, bf16.
+
+Prints ONE JSON line on stdout.  ``value`` is the useful attention FLOP rate
+of the whole step: 4 * head_dim * (allowed (q, k) pairs) * heads * batch per
+step (QK^T and PV only, masked pairs not counted) divided by the measured step
+time.  ``roofline`` covers the dominant kernel (attention), timed with HIP
+events on its own stream; ``cpu_baseline`` is the fp64 oracle on the host
+cores for a bounded sample of query rows of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads as wl  # noqa: E402
+
+METRIC = "attention fwd useful TFLOP/s + % bf16 MFMA peak (4096 img + 1024 text, 32×128)"
+PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 4096 FLOP/clk x 2.4 GHz, dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+DEFAULT_WORKLOAD = "qwen_image21_t1024_i64x64"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_hbm_traffic.json")
+ATTN_SOURCE = os.path.join(ROOT, "diffusion_transformer_joint_token_amd", "csrc", "attn_fwd.hip")
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def useful_pairs(kv_limit: np.ndarray, w: wl.Workload) -> int:
+    """Allowed (q, k) pairs per (batch, head) for the workload's query rows."""
+    if w.mask_mode == "full":
+        return w.n_new * w.seq_len
+    return int(kv_limit[w.prefix_len:].astype(np.int64).sum())
+
+
+def source_sha(path: str) -> str:
+    with open(path, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()
+
+
+def measured_traffic(w: wl.Workload):
+    """HBM bytes per attention launch from the committed rocprofv3 counter runs,
+    or None when they were taken on another kernel source or workload."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != source_sha(ATTN_SOURCE) or rec.get("workload") != w.name:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+class Step:
+    """Device buffers and the launch sequence of one step."""
+
+    def __init__(self, w: wl.Workload, device):
+        import torch
+        import diffusion_transformer_joint_token_amd as dit
+        self.torch, self.dit, self.w = torch, dit, w
+        d = wl.draw(w)
+        self.drawn = d
+
+        def dev(name):
+            bits = np.ascontiguousarray(d.bits[name])
+            if w.dtype == "bf16":
+                return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(device)
+            return torch.from_numpy(bits).to(device)
+        self.q, self.k, self.v = dev("q"), dev("k"), dev("v")
+        self.wq, self.wk = dev("wq"), dev("wk")
+        self.kc = dev("k_cache") if w.prefix_len else None
+        self.vc = dev("v_cache") if w.prefix_len else None
+        mask, self.shapes = wl.sequence_inputs(w)
+        self.mask = torch.from_numpy(mask).to(device)
+        self.meta = dit.TokenMeta.empty(w.seq_len, device)
+        self.qp = torch.empty_like(self.q)
+        self.kp = torch.empty_like(self.k)
+        self.o = torch.empty_like(self.q)
+        self.stream = torch.cuda.current_stream()
+
+    def metadata(self):
+        self.dit.build_token_metadata(self.mask, self.shapes, self.w.pos_mode, out=self.meta)
+
+    def norm_rope(self):
+        P = self.w.prefix_len
+        self.dit.qknorm_rope(self.q, self.k, self.meta.pos_ids[P:], self.w.axes, self.w.eps, self.wq, self.wk,
+                             q_out=self.qp, k_out=self.kp)
+
+    def attention(self):
+        if self.w.prefix_len:
+            self.dit.forward_cached(self.qp, self.kc, self.vc, self.kp, self.v, self.w.mask_mode, self.meta,
+                                    out=self.o)
+        else:
+            self.dit.forward(self.qp, self.kp, self.v, self.w.mask_mode, self.meta, out=self.o)
+
+    def run(self):
+        self.metadata()
+        self.norm_rope()
+        self.attention()
+
+
+def time_gpu(step: Step, steps: int, warmup: int):
+    torch = step.torch
+    for _ in range(warmup):
+        step.run()
+    step.meta.check()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in ev:
+        e[0].record(step.stream)
+        step.metadata()
+        e[1].record(step.stream)
+        step.norm_rope()
+        e[2].record(step.stream)
+        step.attention()
+        e[3].record(step.stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    meta_ms = float(np.mean([a.elapsed_time(b) for a, b, _, _ in ev]))
+    norm_ms = float(np.mean([b.elapsed_time(c) for _, b, c, _ in ev]))
+    attn_ms = [c.elapsed_time(d) for _, _, c, d in ev]
+    step_ms = ev[0][0].elapsed_time(ev[-1][3]) / steps
+    return {"wall_ms_per_step": 1e3 * wall / steps, "step_ms": step_ms, "meta_ms": meta_ms, "norm_ms": norm_ms,
+            "attn_ms_mean": float(np.mean(attn_ms)), "attn_ms_min": float(np.min(attn_ms)),
+            "attn_ms_median": float(np.median(attn_ms))}
+
+
+def cpu_baseline(w: wl.Workload, drawn: wl.Drawn, budget_s: float = 12.0):
+    """The fp64 oracle (as it stands) on the host: norm + rope of the sampled
+    query rows, then their attention rows; rows drawn at random from the
+    workload until the time budget is used.  Scaled to the useful FLOP rate."""
+    import oracle.attention as oatt
+    import oracle.metadata as ometa
+    import oracle.qknorm_rope as oqr
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = len(os.sched_getaffinity(0))
+    mask, shapes = wl.sequence_inputs(w)
+    md = ometa.build_token_metadata(mask, shapes, w.pos_mode)
+    P = w.prefix_len
+    pos = md["pos_ids"][P:]
+    t0 = time.perf_counter()
+    kp = oqr.qknorm_rope(drawn.vals["k"], drawn.vals["wk"], w.eps, pos, w.axes)
+    k_all = np.concatenate([drawn.vals["k_cache"], kp], axis=1) if P else kp
+    v_all = np.concatenate([drawn.vals["v_cache"], drawn.vals["v"]], axis=1) if P else drawn.vals["v"]
+    rng = np.random.default_rng(0)
+    rows_done, pairs = 0, 0
+    chunk = 64
+    while time.perf_counter() - t0 < budget_s:
+        rows = np.sort(rng.choice(w.n_new, size=chunk, replace=False))
+        qp = oqr.qknorm_rope(drawn.vals["q"][:, rows], drawn.vals["wq"], w.eps, pos[rows], w.axes)
+        for j, r in enumerate(rows):
+            oatt.attention(qp[:, j:j + 1], k_all, v_all, md["image_ids"], w.mask_mode, q_offset=P + int(r))
+        rows_done += rows.size
+        lim = md["kv_limit"][P + rows] if w.mask_mode == "block_causal" else np.full(rows.size, w.seq_len)
+        pairs += int(lim.sum())
+    elapsed = time.perf_counter() - t0
+    flops = 4.0 * w.head_dim * pairs * w.heads * w.batch
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": "%d random query rows (all %d heads x batch %d) of %s incl. K norm+rope of every token; "
+                      "%.1f s wall" % (rows_done, w.heads, w.batch, w.name, elapsed),
+            "seconds": elapsed}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=list(wl.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the host oracle timing")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        return 2
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU (none visible)", file=sys.stderr)
+        return 2
+
+    w = wl.WORKLOADS[args.workload]
+    log("workload %s: B=%d H=%d/%d D=%d S=%d (queries %d) mask=%s dtype=%s" % (
+        w.name, w.batch, w.heads, w.kv_heads, w.head_dim, w.seq_len, w.n_new, w.mask_mode, w.dtype))
+    step = Step(w, "cuda")
+    step.run()
+    torch.cuda.synchronize()
+    step.meta.check()
+    kv_limit = step.meta.kv_limit.cpu().numpy()
+    pairs = useful_pairs(kv_limit, w)
+    flops = 4.0 * w.head_dim * pairs * w.heads * w.batch
+    log("useful pairs per (b,h) %d  useful FLOPs/step %.4e" % (pairs, flops))
+
+    t = time_gpu(step, args.steps, args.warmup)
+    log("timing: %s" % json.dumps(t))
+    value = flops / (t["step_ms"] * 1e-3) / 1e12
+    attn_tflops = flops / (t["attn_ms_mean"] * 1e-3) / 1e12
+    elem = 2 if w.dtype == "bf16" else 4
+    norm_bytes = 2 * w.batch * w.n_new * (w.heads + w.kv_heads) * w.head_dim * elem
+
+    roofline = {"bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": attn_tflops / PEAK_BF16_TFLOPS, "traffic": measured_traffic(w),
+                "kernel": "attn_fwd_bf16_kernel<128,4>", "launch_ms_mean": t["attn_ms_mean"],
+                "launch_ms_min": t["attn_ms_min"], "flops_per_launch": flops}
+    line = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": t["step_ms"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "kv_heads": w.kv_heads,
+                   "head_dim": w.head_dim, "seq_len": w.seq_len, "queries": w.n_new, "mask": w.mask_mode,
+                   "rope_axes": list(w.axes), "step": "token metadata + qk-rmsnorm/rope + attention"},
+        "pct_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
+        "attention_only": {"tflops": attn_tflops, "pct_bf16_peak": 100.0 * attn_tflops / PEAK_BF16_TFLOPS,
+                           "ms_mean": t["attn_ms_mean"], "ms_min": t["attn_ms_min"]},
+        "qknorm_rope": {"ms": t["norm_ms"], "gbs": norm_bytes / (t["norm_ms"] * 1e-3) / 1e9,
+                        "frac_hbm": norm_bytes / (t["norm_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                        "bytes": norm_bytes},
+        "token_metadata_ms": t["meta_ms"],
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline: oracle on host cores, ~%.0f s" % args.cpu_budget)
+        cb = cpu_baseline(w, step.drawn, args.cpu_budget)
+        line["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,67 @@
+"""ctypes view of libdit_attn.so (the C ABI declared in include/dit_attn.h).
+
+The library is loaded from this package directory only.  There is no fallback:
+if it has not been built, importing the binding raises, so nothing can silently
+run another implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdit_attn.so")
+
+# Status codes (dit_attn_status).
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_DATA, ERR_HIP = range(7)
+BF16, F32 = 0, 1
+MASK_FULL, MASK_BLOCK_CAUSAL = 0, 1
+POS_CENTERED_FHW, POS_GRID_HW = 0, 1
+MAX_IMAGES = 64
+
+EXPORTED = ("dit_attn_build_token_metadata", "dit_attn_qknorm_rope", "dit_attn_forward",
+            "dit_attn_forward_cached", "dit_attn_status_string")
+
+
+class TokenMetaStruct(ctypes.Structure):
+    _fields_ = [("image_ids", ctypes.c_void_p), ("target_mask", ctypes.c_void_p),
+                ("pos_ids", ctypes.c_void_p), ("kv_limit", ctypes.c_void_p), ("seq_len", ctypes.c_int32)]
+
+
+Strides3 = ctypes.c_int64 * 3
+i32, vp, f32 = ctypes.c_int32, ctypes.c_void_p, ctypes.c_float
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libdit_attn.so is not built (%s); run __graft_entry__.build() or "
+                          "python diffusion_transformer_joint_token_amd/build.py" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.dit_attn_build_token_metadata.argtypes = [vp, i32, ctypes.POINTER(i32), i32, i32,
+                                                  ctypes.POINTER(TokenMetaStruct), vp, vp]
+    lib.dit_attn_qknorm_rope.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                         Strides3, Strides3, Strides3, Strides3, vp, i32,
+                                         ctypes.POINTER(i32), f32, f32, i32, vp]
+    lib.dit_attn_forward.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, Strides3 * 4, i32,
+                                     ctypes.POINTER(TokenMetaStruct), f32, i32, vp]
+    lib.dit_attn_forward_cached.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                            Strides3 * 6, i32, ctypes.POINTER(TokenMetaStruct), f32, i32, vp]
+    for name in EXPORTED[:-1]:
+        getattr(lib, name).restype = ctypes.c_int
+    lib.dit_attn_status_string.argtypes = [i32]
+    lib.dit_attn_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load()
+
+
+class DitAttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib.dit_attn_status_string(status).decode()
+        super().__init__("%s: %s (status %d)" % (where, msg, status))
+
+
+def check(status: int, where: str) -> None:
+    if status != OK:
+        raise DitAttnError(status, where)

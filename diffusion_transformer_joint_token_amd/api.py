@@ -1,0 +1,198 @@
+"""Python binding of the C ABI: the same four entry points on torch tensors.
+
+Argument marshalling only: every step of the computation runs in the gfx950
+kernels of libdit_attn.so.  torch provides device memory and the current HIP
+stream; outputs the caller does not pass are allocated with torch.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from dataclasses import dataclass
+from typing import Optional, Sequence, Tuple, Union
+
+import torch
+
+from . import _lib
+from ._lib import DitAttnError, check, lib
+
+__all__ = ["TokenMeta", "DitAttnError", "dit_attn_build_token_metadata", "dit_attn_qknorm_rope",
+           "dit_attn_forward", "dit_attn_forward_cached", "build_token_metadata", "qknorm_rope", "forward",
+           "forward_cached"]
+
+_POS = {"centered_fhw": _lib.POS_CENTERED_FHW, "grid_hw": _lib.POS_GRID_HW}
+_MASK = {"full": _lib.MASK_FULL, "block_causal": _lib.MASK_BLOCK_CAUSAL}
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return _lib.BF16
+    if t.dtype == torch.float32:
+        return _lib.F32
+    raise DitAttnError(_lib.ERR_UNSUPPORTED, "dtype %s" % t.dtype)
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _bshd_strides(t: torch.Tensor, name: str):
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise DitAttnError(_lib.ERR_SHAPE, "%s must be [B, S, heads, head_dim] with head_dim contiguous" % name)
+    return _lib.Strides3(t.stride(0), t.stride(1), t.stride(2))
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+@dataclass
+class TokenMeta:
+    """Device buffers of the token metadata (one layout for the whole batch)."""
+    image_ids: torch.Tensor    # int32 [S]
+    target_mask: torch.Tensor  # uint8 [S]
+    pos_ids: torch.Tensor      # int32 [S, 3]
+    kv_limit: torch.Tensor     # int32 [S]
+    status: torch.Tensor       # int32 [1]
+
+    @property
+    def seq_len(self) -> int:
+        return self.image_ids.numel()
+
+    def struct(self) -> _lib.TokenMetaStruct:
+        return _lib.TokenMetaStruct(self.image_ids.data_ptr(), self.target_mask.data_ptr(),
+                                    self.pos_ids.data_ptr(), self.kv_limit.data_ptr(), self.seq_len)
+
+    def check(self) -> None:
+        """Synchronise with the producing stream and raise on a data error."""
+        code = int(self.status.item())
+        check(code, "dit_attn_build_token_metadata (device status)")
+
+    @staticmethod
+    def empty(seq_len: int, device) -> "TokenMeta":
+        return TokenMeta(torch.empty(seq_len, dtype=torch.int32, device=device),
+                         torch.empty(seq_len, dtype=torch.uint8, device=device),
+                         torch.empty(seq_len, 3, dtype=torch.int32, device=device),
+                         torch.empty(seq_len, dtype=torch.int32, device=device),
+                         torch.empty(1, dtype=torch.int32, device=device))
+
+
+def dit_attn_build_token_metadata(image_pad_mask: torch.Tensor, img_shapes: Sequence[Sequence[int]],
+                                  pos_mode: Union[str, int] = "centered_fhw", out: Optional[TokenMeta] = None,
+                                  stream=None) -> TokenMeta:
+    mask = image_pad_mask
+    if mask.dtype == torch.bool:
+        mask = mask.view(torch.uint8)
+    if mask.dtype != torch.uint8 or mask.dim() != 1 or not mask.is_contiguous():
+        raise DitAttnError(_lib.ERR_SHAPE, "image_pad_mask must be a contiguous 1-D uint8/bool tensor")
+    S = mask.numel()
+    meta = out if out is not None else TokenMeta.empty(S, mask.device)
+    flat = [int(v) for shp in img_shapes for v in shp]
+    if len(flat) != 3 * len(img_shapes):
+        raise DitAttnError(_lib.ERR_SHAPE, "img_shapes entries must be (frames, height, width)")
+    shapes = (ctypes.c_int32 * max(1, len(flat)))(*flat)
+    mode = _POS[pos_mode] if isinstance(pos_mode, str) else int(pos_mode)
+    ms = meta.struct()
+    st = lib.dit_attn_build_token_metadata(mask.data_ptr(), S, shapes, len(img_shapes), mode, ctypes.byref(ms),
+                                           meta.status.data_ptr(), _stream(stream))
+    check(st, "dit_attn_build_token_metadata")
+    return meta
+
+
+def dit_attn_qknorm_rope(q: torch.Tensor, k: torch.Tensor, pos_ids: torch.Tensor, axes_dims: Sequence[int],
+                         eps: float, q_weight: Optional[torch.Tensor] = None,
+                         k_weight: Optional[torch.Tensor] = None, rope_theta: float = 10000.0,
+                         q_out: Optional[torch.Tensor] = None, k_out: Optional[torch.Tensor] = None,
+                         inplace: bool = False, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    if inplace:
+        q_out, k_out = q, k
+    if q_out is None:
+        q_out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if k_out is None:
+        k_out = torch.empty_like(k, memory_format=torch.contiguous_format)
+    B, S, H, D = q.shape
+    Hk = k.shape[2]
+    if k.shape[0] != B or k.shape[1] != S or k.shape[3] != D or q_out.shape != q.shape or k_out.shape != k.shape:
+        raise DitAttnError(_lib.ERR_SHAPE, "q/k/out shapes disagree")
+    if pos_ids.dtype != torch.int32 or not pos_ids.is_contiguous() or pos_ids.numel() < 3 * S:
+        raise DitAttnError(_lib.ERR_SHAPE, "pos_ids must be contiguous int32 [S, 3]")
+    for w in (q_weight, k_weight):
+        if w is not None and (w.dtype != q.dtype or w.numel() != D or not w.is_contiguous()):
+            raise DitAttnError(_lib.ERR_SHAPE, "norm weights must be contiguous [head_dim] in the input dtype")
+    dt = _dtype_code(q)
+    if k.dtype != q.dtype or q_out.dtype != q.dtype or k_out.dtype != q.dtype:
+        raise DitAttnError(_lib.ERR_UNSUPPORTED, "mixed dtypes")
+    axes = (ctypes.c_int32 * len(axes_dims))(*[int(a) for a in axes_dims])
+    st = lib.dit_attn_qknorm_rope(q.data_ptr(), k.data_ptr(), q_out.data_ptr(), k_out.data_ptr(), _ptr(q_weight),
+                                  _ptr(k_weight), B, S, H, Hk, D, _bshd_strides(q, "q"), _bshd_strides(k, "k"),
+                                  _bshd_strides(q_out, "q_out"), _bshd_strides(k_out, "k_out"), pos_ids.data_ptr(),
+                                  len(axes_dims), axes, float(rope_theta), float(eps), dt, _stream(stream))
+    check(st, "dit_attn_qknorm_rope")
+    return q_out, k_out
+
+
+def _lse_buffer(return_lse: bool, B: int, H: int, S: int, device) -> Optional[torch.Tensor]:
+    return torch.empty(B, H, S, dtype=torch.float32, device=device) if return_lse else None
+
+
+def dit_attn_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask_mode: Union[str, int] = "full",
+                     meta: Optional[TokenMeta] = None, softmax_scale: Optional[float] = None,
+                     out: Optional[torch.Tensor] = None, return_lse: bool = False, stream=None):
+    B, S, H, D = q.shape
+    Hk = k.shape[2]
+    if k.shape != (B, S, Hk, D) or v.shape != (B, S, Hk, D):
+        raise DitAttnError(_lib.ERR_SHAPE, "k/v must be [B, S, H_kv, D] matching q")
+    o = out if out is not None else torch.empty_like(q, memory_format=torch.contiguous_format)
+    lse = _lse_buffer(return_lse, B, H, S, q.device)
+    strides = (_lib.Strides3 * 4)(_bshd_strides(q, "q"), _bshd_strides(k, "k"), _bshd_strides(v, "v"),
+                                  _bshd_strides(o, "out"))
+    dt = _dtype_code(q)
+    if any(t.dtype != q.dtype for t in (k, v, o)):
+        raise DitAttnError(_lib.ERR_UNSUPPORTED, "mixed dtypes")
+    mode = _MASK[mask_mode] if isinstance(mask_mode, str) else int(mask_mode)
+    ms = meta.struct() if meta is not None else None
+    scale = 0.0 if softmax_scale is None else float(softmax_scale)
+    st = lib.dit_attn_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _ptr(lse), B, S, H, Hk, D,
+                              strides, mode, ctypes.byref(ms) if ms is not None else None, scale, dt,
+                              _stream(stream))
+    check(st, "dit_attn_forward")
+    return (o, lse) if return_lse else o
+
+
+def dit_attn_forward_cached(q_new: torch.Tensor, k_cache: Optional[torch.Tensor], v_cache: Optional[torch.Tensor],
+                            k_new: torch.Tensor, v_new: torch.Tensor, mask_mode: Union[str, int] = "block_causal",
+                            meta: Optional[TokenMeta] = None, softmax_scale: Optional[float] = None,
+                            out: Optional[torch.Tensor] = None, return_lse: bool = False, stream=None):
+    B, S_new, H, D = q_new.shape
+    Hk = k_new.shape[2]
+    P = 0 if k_cache is None else k_cache.shape[1]
+    if k_new.shape != (B, S_new, Hk, D) or v_new.shape != (B, S_new, Hk, D):
+        raise DitAttnError(_lib.ERR_SHAPE, "k_new/v_new must be [B, S_new, H_kv, D]")
+    if P > 0 and (k_cache.shape != (B, P, Hk, D) or v_cache is None or v_cache.shape != (B, P, Hk, D)):
+        raise DitAttnError(_lib.ERR_SHAPE, "k_cache/v_cache must be [B, P, H_kv, D]")
+    o = out if out is not None else torch.empty_like(q_new, memory_format=torch.contiguous_format)
+    lse = _lse_buffer(return_lse, B, H, S_new, q_new.device)
+    zero = _lib.Strides3(0, 0, 0)
+    strides = (_lib.Strides3 * 6)(_bshd_strides(q_new, "q_new"),
+                                  _bshd_strides(k_cache, "k_cache") if P > 0 else zero,
+                                  _bshd_strides(v_cache, "v_cache") if P > 0 else zero,
+                                  _bshd_strides(k_new, "k_new"), _bshd_strides(v_new, "v_new"),
+                                  _bshd_strides(o, "out"))
+    dt = _dtype_code(q_new)
+    mode = _MASK[mask_mode] if isinstance(mask_mode, str) else int(mask_mode)
+    ms = meta.struct() if meta is not None else None
+    scale = 0.0 if softmax_scale is None else float(softmax_scale)
+    st = lib.dit_attn_forward_cached(q_new.data_ptr(), _ptr(k_cache) if P > 0 else None,
+                                     _ptr(v_cache) if P > 0 else None, k_new.data_ptr(), v_new.data_ptr(),
+                                     o.data_ptr(), _ptr(lse), B, P, S_new, H, Hk, D, strides, mode,
+                                     ctypes.byref(ms) if ms is not None else None, scale, dt, _stream(stream))
+    check(st, "dit_attn_forward_cached")
+    return (o, lse) if return_lse else o
+
+
+build_token_metadata = dit_attn_build_token_metadata
+qknorm_rope = dit_attn_qknorm_rope
+forward = dit_attn_forward
+forward_cached = dit_attn_forward_cached

@@ -1,0 +1,237 @@
+// C-ABI entry points: argument validation on the host, then one kernel launch
+// on the caller's stream.  Nothing here allocates, frees or synchronises.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/dit_attn.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = 128;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Every row start must stay 16-byte aligned: base pointer and each stride.
+bool rows_aligned(const void* p, const int64_t st[3], int elem) {
+  if (!aligned16(p)) return false;
+  for (int i = 0; i < 3; ++i)
+    if ((st[i] * elem) % 16 != 0) return false;
+  return true;
+}
+
+bool strides_ok(const int64_t st[3]) {
+  for (int i = 0; i < 3; ++i)
+    if (st[i] < 0) return false;
+  return true;
+}
+
+int elem_size(int32_t dtype) { return dtype == DIT_ATTN_BF16 ? 2 : 4; }
+
+}  // namespace
+
+extern "C" {
+
+const char* dit_attn_status_string(int32_t status) {
+  switch (status) {
+    case DIT_ATTN_OK: return "ok";
+    case DIT_ATTN_ERR_NULL: return "a required pointer is NULL";
+    case DIT_ATTN_ERR_SHAPE: return "sizes are inconsistent or out of range";
+    case DIT_ATTN_ERR_UNSUPPORTED: return "request not supported by this build";
+    case DIT_ATTN_ERR_ALIGN: return "pointer or stride breaks 16-byte row alignment";
+    case DIT_ATTN_ERR_DATA: return "device data break the layout contract";
+    case DIT_ATTN_ERR_HIP: return "HIP runtime or launch failure";
+    default: return "unknown status";
+  }
+}
+
+int dit_attn_build_token_metadata(const uint8_t* image_pad_mask, int32_t seq_len, const int32_t* img_shapes,
+                                  int32_t n_img, int32_t pos_mode, const dit_attn_token_meta* meta,
+                                  int32_t* status_dev, void* stream) {
+  if (!image_pad_mask || !meta || !status_dev || (n_img > 0 && !img_shapes)) return DIT_ATTN_ERR_NULL;
+  if (!meta->image_ids || !meta->target_mask || !meta->pos_ids || !meta->kv_limit) return DIT_ATTN_ERR_NULL;
+  if (seq_len < 1 || meta->seq_len != seq_len) return DIT_ATTN_ERR_SHAPE;
+  if (n_img < 0 || n_img > DIT_ATTN_MAX_IMAGES) return DIT_ATTN_ERR_SHAPE;
+  if (pos_mode != DIT_ATTN_POS_CENTERED_FHW && pos_mode != DIT_ATTN_POS_GRID_HW) return DIT_ATTN_ERR_UNSUPPORTED;
+
+  dit::TokenMetaArgs a{};
+  a.seq_len = seq_len;
+  a.n_img = n_img;
+  a.pos_mode = pos_mode;
+  int64_t total = 0, frames = 0;
+  int32_t max_coord = -1;
+  a.cum[0] = 0;
+  for (int b = 0; b < n_img; ++b) {
+    const int64_t f = img_shapes[3 * b], h = img_shapes[3 * b + 1], w = img_shapes[3 * b + 2];
+    if (f < 1 || h < 1 || w < 1) return DIT_ATTN_ERR_SHAPE;
+    if (f * h * w > seq_len) return DIT_ATTN_ERR_SHAPE;
+    if (pos_mode == DIT_ATTN_POS_CENTERED_FHW && ((h & 1) || (w & 1))) return DIT_ATTN_ERR_SHAPE;
+    if (pos_mode == DIT_ATTN_POS_GRID_HW && f != 1) return DIT_ATTN_ERR_SHAPE;
+    a.shape[b][0] = (int32_t)f;
+    a.shape[b][1] = (int32_t)h;
+    a.shape[b][2] = (int32_t)w;
+    a.frame_off[b] = (int32_t)frames;
+    total += f * h * w;
+    if (total > seq_len) return DIT_ATTN_ERR_SHAPE;
+    a.cum[b + 1] = (int32_t)total;
+    frames += f;
+    const int64_t mc = std::max<int64_t>(frames - 1, std::max<int64_t>(h / 2 - 1, w / 2 - 1));
+    if (mc > max_coord) max_coord = (int32_t)mc;
+  }
+  a.max_vid = n_img > 0 ? max_coord + 1 : 0;
+  hipError_t e = dit::launch_token_meta(image_pad_mask, a, meta->image_ids, meta->target_mask, meta->pos_ids,
+                                        meta->kv_limit, status_dev, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DIT_ATTN_OK : DIT_ATTN_ERR_HIP;
+}
+
+int dit_attn_qknorm_rope(const void* q, const void* k, void* q_out, void* k_out, const void* q_weight,
+                         const void* k_weight, int32_t B, int32_t S, int32_t H, int32_t H_kv, int32_t D,
+                         const int64_t q_strides[3], const int64_t k_strides[3], const int64_t qo_strides[3],
+                         const int64_t ko_strides[3], const int32_t* pos_ids, int32_t n_axes,
+                         const int32_t* axes_dims, float rope_theta, float eps, int32_t dtype, void* stream) {
+  if (B < 0 || S < 0) return DIT_ATTN_ERR_SHAPE;
+  if (B == 0 || S == 0) return DIT_ATTN_OK;  // nothing to do; no pointer is read
+  if (!q || !k || !q_out || !k_out || !pos_ids || !axes_dims || !q_strides || !k_strides || !qo_strides ||
+      !ko_strides)
+    return DIT_ATTN_ERR_NULL;
+  if (dtype != DIT_ATTN_BF16 && dtype != DIT_ATTN_F32) return DIT_ATTN_ERR_UNSUPPORTED;
+  if (B < 0 || S < 0 || H < 1 || H_kv < 1) return DIT_ATTN_ERR_SHAPE;
+  if (B > 65535) return DIT_ATTN_ERR_UNSUPPORTED;
+  const int chunk = dtype == DIT_ATTN_BF16 ? 8 : 4;
+  if (D < 8 || D > kMaxDim || D % chunk != 0) return DIT_ATTN_ERR_UNSUPPORTED;
+  if (n_axes < 1 || n_axes > 3) return DIT_ATTN_ERR_SHAPE;
+  int sum = 0;
+  for (int i = 0; i < n_axes; ++i) {
+    if (axes_dims[i] < 0 || (axes_dims[i] & 1)) return DIT_ATTN_ERR_SHAPE;
+    sum += axes_dims[i];
+  }
+  if (sum != D) return DIT_ATTN_ERR_SHAPE;
+  if (!(rope_theta > 0.f) || !std::isfinite(rope_theta) || !(eps >= 0.f) || !std::isfinite(eps))
+    return DIT_ATTN_ERR_SHAPE;
+  if (!strides_ok(q_strides) || !strides_ok(k_strides) || !strides_ok(qo_strides) || !strides_ok(ko_strides))
+    return DIT_ATTN_ERR_SHAPE;
+  const int es = elem_size(dtype);
+  if (!rows_aligned(q, q_strides, es) || !rows_aligned(k, k_strides, es) || !rows_aligned(q_out, qo_strides, es) ||
+      !rows_aligned(k_out, ko_strides, es) || (q_weight && !aligned16(q_weight)) ||
+      (k_weight && !aligned16(k_weight)))
+    return DIT_ATTN_ERR_ALIGN;
+
+  dit::QkNormRopeArgs a{};
+  a.q = q;
+  a.k = k;
+  a.qo = q_out;
+  a.ko = k_out;
+  a.wq = q_weight;
+  a.wk = k_weight;
+  a.pos = pos_ids;
+  for (int i = 0; i < 3; ++i) {
+    a.qs[i] = q_strides[i];
+    a.ks[i] = k_strides[i];
+    a.qos[i] = qo_strides[i];
+    a.kos[i] = ko_strides[i];
+  }
+  a.B = B;
+  a.S = S;
+  a.H = H;
+  a.Hk = H_kv;
+  a.D = D;
+  a.eps = eps;
+  int p = 0;
+  for (int ax = 0; ax < n_axes; ++ax) {
+    const int da = axes_dims[ax];
+    for (int j = 0; j < da / 2; ++j, ++p) {
+      a.omega[p] = std::pow((double)rope_theta, -2.0 * j / da);
+      a.pair_axis[p] = ax;
+    }
+  }
+  hipError_t e = dit::launch_qknorm_rope(a, dtype, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DIT_ATTN_OK : DIT_ATTN_ERR_HIP;
+}
+
+static int attention_common(const void* q, const void* kc, const void* vc, const void* kn, const void* vn, void* o,
+                            float* lse, int32_t B, int32_t P, int32_t S_new, int32_t H, int32_t H_kv, int32_t D,
+                            const int64_t* const st[6], int32_t mask_mode, const dit_attn_token_meta* meta,
+                            float softmax_scale, int32_t dtype, void* stream) {
+  if (dtype != DIT_ATTN_BF16 && dtype != DIT_ATTN_F32) return DIT_ATTN_ERR_UNSUPPORTED;
+  if (mask_mode != DIT_ATTN_MASK_FULL && mask_mode != DIT_ATTN_MASK_BLOCK_CAUSAL) return DIT_ATTN_ERR_UNSUPPORTED;
+  if (B < 0 || P < 0 || S_new < 0 || H < 1 || H_kv < 1 || H % H_kv != 0) return DIT_ATTN_ERR_SHAPE;
+  const int chunk = dtype == DIT_ATTN_BF16 ? 8 : 4;
+  if (D < 8 || D > kMaxDim || D % chunk != 0) return DIT_ATTN_ERR_UNSUPPORTED;
+  if ((int64_t)P + S_new > INT32_MAX) return DIT_ATTN_ERR_SHAPE;
+  for (int i = 0; i < 6; ++i)
+    if (!strides_ok(st[i])) return DIT_ATTN_ERR_SHAPE;
+  const int32_t* kv_limit = nullptr;
+  if (mask_mode == DIT_ATTN_MASK_BLOCK_CAUSAL) {
+    if (!meta || !meta->kv_limit) return DIT_ATTN_ERR_NULL;
+    if (meta->seq_len != P + S_new) return DIT_ATTN_ERR_SHAPE;
+    kv_limit = meta->kv_limit;
+  } else if (meta && meta->seq_len != P + S_new) {
+    return DIT_ATTN_ERR_SHAPE;
+  }
+  const int es = elem_size(dtype);
+  if (!rows_aligned(q, st[0], es) || !rows_aligned(kn, st[3], es) || !rows_aligned(vn, st[4], es) ||
+      !rows_aligned(o, st[5], es))
+    return DIT_ATTN_ERR_ALIGN;
+  if (P > 0 && (!rows_aligned(kc, st[1], es) || !rows_aligned(vc, st[2], es))) return DIT_ATTN_ERR_ALIGN;
+  if (B == 0 || S_new == 0) return DIT_ATTN_OK;
+  const int64_t blocks = ((int64_t)S_new + 127) / 128 * B * H;
+  if (blocks > INT32_MAX || ((int64_t)S_new + 63) / 64 * B * H > INT32_MAX) return DIT_ATTN_ERR_UNSUPPORTED;
+
+  dit::AttnArgs a{};
+  a.q = q;
+  a.kc = P > 0 ? kc : kn;
+  a.vc = P > 0 ? vc : vn;
+  a.kn = kn;
+  a.vn = vn;
+  a.o = o;
+  a.lse = lse;
+  a.kv_limit = kv_limit;
+  for (int i = 0; i < 3; ++i) {
+    a.qs[i] = st[0][i];
+    a.kcs[i] = P > 0 ? st[1][i] : st[3][i];
+    a.vcs[i] = P > 0 ? st[2][i] : st[4][i];
+    a.kns[i] = st[3][i];
+    a.vns[i] = st[4][i];
+    a.os[i] = st[5][i];
+  }
+  a.B = B;
+  a.H = H;
+  a.Hk = H_kv;
+  a.D = D;
+  a.P = P;
+  a.Snew = S_new;
+  a.Sk = P + S_new;
+  a.scale = (softmax_scale > 0.f && std::isfinite(softmax_scale)) ? softmax_scale : (float)(1.0 / std::sqrt((double)D));
+  hipError_t e = dit::launch_attention(a, dtype, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DIT_ATTN_OK : DIT_ATTN_ERR_HIP;
+}
+
+int dit_attn_forward(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B, int32_t S,
+                     int32_t H, int32_t H_kv, int32_t D, const int64_t strides[4][3], int32_t mask_mode,
+                     const dit_attn_token_meta* meta, float softmax_scale, int32_t dtype, void* stream) {
+  if (B < 0 || S < 0) return DIT_ATTN_ERR_SHAPE;
+  if (B == 0 || S == 0) return DIT_ATTN_OK;  // nothing to do; no pointer is read
+  if (!q || !k || !v || !o || !strides) return DIT_ATTN_ERR_NULL;
+  const int64_t* st[6] = {strides[0], strides[1], strides[2], strides[1], strides[2], strides[3]};
+  return attention_common(q, k, v, k, v, o, lse, B, 0, S, H, H_kv, D, st, mask_mode, meta, softmax_scale, dtype,
+                          stream);
+}
+
+int dit_attn_forward_cached(const void* q_new, const void* k_cache, const void* v_cache, const void* k_new,
+                            const void* v_new, void* o, float* lse, int32_t B, int32_t P, int32_t S_new, int32_t H,
+                            int32_t H_kv, int32_t D, const int64_t strides[6][3], int32_t mask_mode,
+                            const dit_attn_token_meta* meta, float softmax_scale, int32_t dtype, void* stream) {
+  if (B < 0 || P < 0 || S_new < 0) return DIT_ATTN_ERR_SHAPE;
+  if (B == 0 || S_new == 0) return DIT_ATTN_OK;  // nothing to do; no pointer is read
+  if (!q_new || !k_new || !v_new || !o || !strides) return DIT_ATTN_ERR_NULL;
+  if (P > 0 && (!k_cache || !v_cache)) return DIT_ATTN_ERR_NULL;
+  const int64_t* st[6] = {strides[0], strides[1], strides[2], strides[3], strides[4], strides[5]};
+  return attention_common(q_new, k_cache, v_cache, k_new, v_new, o, lse, B, P, S_new, H, H_kv, D, st, mask_mode,
+                          meta, softmax_scale, dtype, stream);
+}
+
+}  // extern "C"

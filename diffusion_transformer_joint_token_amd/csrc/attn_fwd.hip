@@ -1,0 +1,403 @@
+// Masked softmax attention over the joint text+image sequence (gfx950).
+//
+// QwenImage21Transformer2DModel API page: a query attends a key when
+// q_idx >= kv_idx or both lie in the same image block (block-causal), or every
+// key (full).  For contiguous blocks the allowed keys of query q are exactly
+// the prefix [0, kv_limit[q]) with kv_limit non-decreasing along the
+// sequence, so a tile of queries x keys is either fully allowed, fully masked
+// or needs a per-element test only near its diagonal; masked tiles are never
+// loaded or computed.  The same page's cached mode ("kv_cache" of the
+// timestep-independent prefix) is the same loop with keys [0, P) read from the
+// cache and keys [P, P + S_new) from the new tokens.  GQA: query head h reads
+// KV head h / (H / H_kv) (NucleusMoE-Image article, section 6.3).
+//
+// bf16 kernel layout (one work-group = NW waves = 32*NW query rows of one
+// (batch, head); key tiles of 64):
+//  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: A = K rows from LDS, B = Q^T kept
+//    in registers for the whole kernel.  The accumulator then gives every lane
+//    one query column and 16 keys, so the online-softmax max/sum are in-lane
+//    reductions plus one exchange with the lane 32 apart (v_permlane32_swap).
+//  * O^T += V^T P^T on the same MFMA: B = P^T straight from the S^T accumulator
+//    (rounded to bf16), A = V^T read from the row-major V tile with
+//    ds_read_b64_tr_b16, whose 16-lane transpose delivers 4 consecutive keys of
+//    one head channel per lane in exactly the key order of the accumulator.
+//  * K and V tiles move global -> LDS with direct 16-byte LDS loads (no VGPR
+//    staging), double-buffered; 16-byte chunks are XOR-swizzled per row so both
+//    the K reads (16 rows, same chunk) and the transposed V reads (4 rows x 4
+//    chunks) hit distinct banks.
+//  * Softmax in the exp2 domain with the scale folded into one FMA; the running
+//    max is only moved when a row's new maximum exceeds it by more than 8
+//    (log2 units), so O is rarely rescaled and probabilities stay <= 2^8.
+//  * Work-groups are ordered heaviest query tile first and mapped so that all
+//    query tiles of one (batch, head) share an XCD (and its L2).
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace dit {
+
+namespace {
+
+constexpr int kTileN = 64;        // keys per tile
+constexpr int kRowBytes = 256;    // LDS bytes per key row (16 chunks of 16 B)
+constexpr int kTileBytes = kTileN * kRowBytes;
+constexpr float kLazyRescale = 8.0f;  // log2 units
+
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+
+// Work-group index -> (batch*head, query tile), heaviest query tile first and
+// all tiles of one (batch, head) on one XCD (work-groups are dealt to the 8
+// XCDs round-robin).
+__device__ __forceinline__ void map_block(int id, int nblocks, int n_qtiles, int& bh, int& qtile) {
+  const int per = nblocks >> 3;
+  int logical = id;
+  if (id < per * 8) logical = (id & 7) * per + (id >> 3);
+  bh = logical / n_qtiles;
+  qtile = n_qtiles - 1 - (logical - bh * n_qtiles);
+}
+
+template <int DP, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
+  static_assert(DP % 32 == 0 && DP <= 128, "padded head dim");
+  constexpr int KSTEPS = DP / 16;  // QK^T contraction steps
+  constexpr int MBLK = DP / 32;    // 32-channel blocks of O^T
+  constexpr int CHUNKS = DP / 8;   // 16-byte chunks per key row actually used
+  constexpr int LOADS = (kTileN * 16) / (NW * 64);  // LDS-load instructions per wave per tile
+
+  __shared__ __attribute__((aligned(1024))) char smem[2][2][kTileBytes];  // [buffer][K|V]
+  __shared__ int s_lim[NW];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 5;  // k-group of the MFMA operands
+  const int n_qtiles = (a.Snew + 32 * NW - 1) / (32 * NW);
+  int bh, qtile;
+  map_block(blockIdx.x, gridDim.x, n_qtiles, bh, qtile);
+  const int h = bh % a.H;
+  const int b = bh / a.H;
+  const int kvh = h / (a.H / a.Hk);
+  const int Sk = a.Sk;
+
+  // This lane's query row and its key bound.
+  const int qrow = qtile * 32 * NW + wave * 32 + (lane & 31);
+  const bool row_ok = qrow < a.Snew;
+  const int qclamp = row_ok ? qrow : a.Snew - 1;
+  const int lim = a.kv_limit ? a.kv_limit[a.P + qclamp] : Sk;
+  int wlim_max = lim, wlim_min = lim;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    wlim_max = max(wlim_max, __shfl_xor(wlim_max, m, 64));
+    wlim_min = min(wlim_min, __shfl_xor(wlim_min, m, 64));
+  }
+  if (lane == 0) s_lim[wave] = wlim_max;
+
+  // Q^T operand: lane holds query (lane & 31), channels 16*ks + 8*g .. +7.
+  bf16x8 qreg[KSTEPS];
+  {
+    const __bf16* qp = reinterpret_cast<const __bf16*>(a.q) + b * a.qs[0] + (int64_t)qclamp * a.qs[1] + h * a.qs[2];
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const int d0 = 16 * ks + 8 * g;
+      if (d0 < a.D && row_ok)
+        qreg[ks] = *reinterpret_cast<const bf16x8*>(qp + d0);
+      else
+        qreg[ks] = bf16x8{};
+    }
+  }
+  __syncthreads();
+  int wg_lim = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) wg_lim = max(wg_lim, s_lim[w]);
+  const int n_tiles = (wg_lim + kTileN - 1) / kTileN;
+
+  // Global -> LDS loader.  Position p = 64*(i*NW + wave) + lane of a tile is
+  // row p/16, physical chunk p%16, which holds logical chunk (p%16) ^ swz(row).
+  const __bf16* kc = reinterpret_cast<const __bf16*>(a.kc) + b * a.kcs[0] + kvh * a.kcs[2];
+  const __bf16* vc = reinterpret_cast<const __bf16*>(a.vc) + b * a.vcs[0] + kvh * a.vcs[2];
+  const __bf16* kn = reinterpret_cast<const __bf16*>(a.kn) + b * a.kns[0] + kvh * a.kns[2];
+  const __bf16* vn = reinterpret_cast<const __bf16*>(a.vn) + b * a.vns[0] + kvh * a.vns[2];
+  const int dchunks = a.D / 8;
+  auto issue_tile = [&](int t, int buf) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int p = 64 * (i * NW + wave) + lane;
+      const int row = p >> 4;
+      const int c = (p & 15) ^ swz(row);
+      if (c < CHUNKS) {
+        int key = t * kTileN + row;
+        key = key < Sk ? key : Sk - 1;
+        const int cs = c < dchunks ? c : 0;  // padding channels: any finite data (Q is zero there)
+        const __bf16* ks;
+        const __bf16* vs;
+        if (key < a.P) {
+          ks = kc + (int64_t)key * a.kcs[1];
+          vs = vc + (int64_t)key * a.vcs[1];
+        } else {
+          ks = kn + (int64_t)(key - a.P) * a.kns[1];
+          vs = vn + (int64_t)(key - a.P) * a.vns[1];
+        }
+        lds_void* kdst = (lds_void*)(&smem[buf][0][64 * 16 * (i * NW + wave)]);
+        lds_void* vdst = (lds_void*)(&smem[buf][1][64 * 16 * (i * NW + wave)]);
+        __builtin_amdgcn_global_load_lds(ks + 8 * cs, kdst, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vs + 8 * cs, vdst, 16, 0, 0);
+      }
+    }
+  };
+
+  f32x16 oacc[MBLK];
+#pragma unroll
+  for (int mb = 0; mb < MBLK; ++mb) oacc[mb] = f32x16{};
+  const float c2 = a.scale * 1.4426950408889634f;  // scale * log2(e)
+  float m_cur = -INFINITY;  // running max of the raw logits (unscaled)
+  float l_part = 0.f;       // this lane's share of the row sum
+
+  if (n_tiles > 0) issue_tile(0, 0);
+  for (int t = 0; t < n_tiles; ++t) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (t + 1 < n_tiles) issue_tile(t + 1, (t + 1) & 1);
+    const int k0 = t * kTileN;
+    if (k0 >= wlim_max) continue;  // wave-uniform: nothing allowed in this tile
+    const char* kt = smem[t & 1][0];
+    const char* vt = smem[t & 1][1];
+
+    // S^T for two 32-key blocks.
+    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int row = 32 * kb + (lane & 31);
+        const int pc = (2 * ks + g) ^ swz(row);
+        const bf16x8 kop = *reinterpret_cast<const bf16x8*>(kt + row * kRowBytes + pc * 16);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[ks], sacc[kb], 0, 0, 0);
+      }
+    }
+
+    // Mask near the diagonal (or past the end of the keys).
+    if (k0 + kTileN > wlim_min) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = k0 + 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
+          if (key >= lim) sacc[kb][i] = -INFINITY;
+        }
+      }
+    }
+
+    // Row max (this lane's 32 keys, then the partner lane's 32).
+    float mx = sacc[0][0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[0][i]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[1][i]);
+    mx = max_with_partner32(mx);
+    const bool grow = (mx - m_cur) * c2 > kLazyRescale;
+    if (__any(grow)) {
+      // Only the rows that grew move their max (alpha = 1 elsewhere), so a
+      // row's result never depends on the other rows of its wave.
+      const float m_new = grow ? mx : m_cur;
+      const float alpha = __builtin_amdgcn_exp2f((m_cur - m_new) * c2);
+      l_part *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < MBLK; ++mb) oacc[mb] *= alpha;
+      m_cur = m_new;
+    }
+    // A row with no allowed key so far keeps m = -inf; its p must be 0, not NaN.
+    const float mc = (m_cur == -INFINITY) ? 0.f : m_cur * c2;
+
+    // P = exp2(s * c2 - m * c2), row sums, bf16 B operands for PV.
+    bf16x8 pop[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        float pv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          pv[j] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][8 * half + j], c2, -mc));
+          l_part += pv[j];
+        }
+        u32x4 w;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[j] = pack_bf16x2(pv[2 * j], pv[2 * j + 1]);
+        pop[kb][half] = __builtin_bit_cast(bf16x8, w);
+      }
+    }
+
+    // O^T += V^T P^T.
+    const int G = lane >> 4;
+    const int il = lane & 15;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int key_lo = 32 * kb + 16 * half + 4 * (G >> 1) + (il >> 2);
+        const int key_hi = key_lo + 8;
+#pragma unroll
+        for (int mb = 0; mb < MBLK; ++mb) {
+          const int d = 32 * mb + 16 * (G & 1) + 4 * (il & 3);
+          const int c = d >> 3;
+          const int hb = ((d >> 2) & 1) * 8;
+          const lds_void* p_lo = (const lds_void*)(vt + key_lo * kRowBytes + ((c ^ swz(key_lo)) << 4) + hb);
+          const lds_void* p_hi = (const lds_void*)(vt + key_hi * kRowBytes + ((c ^ swz(key_hi)) << 4) + hb);
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p_lo);
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p_hi);
+          const u32x4 vw = {__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                            __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
+          oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vw), pop[kb][half],
+                                                            oacc[mb], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // Normalise and store: lane holds query (lane & 31), channels
+  // 32*mb + 8*(i/4) + 4*g + (i%4).
+  const float l_tot = sum_with_partner32(l_part);
+  const float inv = 1.0f / l_tot;
+  if (row_ok) {
+    __bf16* op = reinterpret_cast<__bf16*>(a.o) + b * a.os[0] + (int64_t)qrow * a.os[1] + h * a.os[2];
+#pragma unroll
+    for (int mb = 0; mb < MBLK; ++mb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int d = 32 * mb + 8 * r + 4 * g;
+        if (d < a.D) {
+          u32x2 w;
+          w[0] = pack_bf16x2(oacc[mb][4 * r + 0] * inv, oacc[mb][4 * r + 1] * inv);
+          w[1] = pack_bf16x2(oacc[mb][4 * r + 2] * inv, oacc[mb][4 * r + 3] * inv);
+          *reinterpret_cast<u32x2*>(op + d) = w;
+        }
+      }
+    }
+    if (a.lse != nullptr && g == 0)
+      a.lse[((int64_t)b * a.H + h) * a.Snew + qrow] = m_cur * a.scale + logf(l_tot);
+  }
+}
+
+// fp32 path: one thread per query row, K/V tiles of 32 keys in LDS, exact
+// online softmax per tile.  Used for fp32 inputs (parity-grade small shapes).
+template <int DP>
+__global__ __launch_bounds__(64) void attn_fwd_f32_kernel(AttnArgs a) {
+  constexpr int TK = 32;
+  __shared__ float sk[TK][DP];
+  __shared__ float sv[TK][DP];
+  const int tid = threadIdx.x;
+  const int n_qtiles = (a.Snew + 63) / 64;
+  const int bh = blockIdx.x / n_qtiles;
+  const int qt = blockIdx.x % n_qtiles;
+  const int h = bh % a.H;
+  const int b = bh / a.H;
+  const int kvh = h / (a.H / a.Hk);
+  const int qrow = qt * 64 + tid;
+  const bool row_ok = qrow < a.Snew;
+  const int qclamp = row_ok ? qrow : a.Snew - 1;
+  const int lim = a.kv_limit ? a.kv_limit[a.P + qclamp] : a.Sk;
+  int wlim = lim;
+  for (int m = 32; m >= 1; m >>= 1) wlim = max(wlim, __shfl_xor(wlim, m, 64));
+
+  float q[DP], o[DP];
+  const float* qp = reinterpret_cast<const float*>(a.q) + b * a.qs[0] + (int64_t)qclamp * a.qs[1] + h * a.qs[2];
+#pragma unroll
+  for (int d = 0; d < DP; ++d) {
+    q[d] = d < a.D ? qp[d] : 0.f;
+    o[d] = 0.f;
+  }
+  float m_cur = -INFINITY, l = 0.f;
+  for (int k0 = 0; k0 < wlim; k0 += TK) {
+    __syncthreads();
+    for (int e = tid; e < TK * DP; e += 64) {
+      const int r = e / DP, d = e % DP;
+      int key = k0 + r;
+      key = key < a.Sk ? key : a.Sk - 1;
+      float kvv = 0.f, vvv = 0.f;
+      if (d < a.D) {
+        if (key < a.P) {
+          kvv = reinterpret_cast<const float*>(a.kc)[b * a.kcs[0] + (int64_t)key * a.kcs[1] + kvh * a.kcs[2] + d];
+          vvv = reinterpret_cast<const float*>(a.vc)[b * a.vcs[0] + (int64_t)key * a.vcs[1] + kvh * a.vcs[2] + d];
+        } else {
+          const int kk = key - a.P;
+          kvv = reinterpret_cast<const float*>(a.kn)[b * a.kns[0] + (int64_t)kk * a.kns[1] + kvh * a.kns[2] + d];
+          vvv = reinterpret_cast<const float*>(a.vn)[b * a.vns[0] + (int64_t)kk * a.vns[1] + kvh * a.vns[2] + d];
+        }
+      }
+      sk[r][d] = kvv;
+      sv[r][d] = vvv;
+    }
+    __syncthreads();
+    float s[TK];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < TK; ++j) {
+      float acc = 0.f;
+#pragma unroll
+      for (int d = 0; d < DP; ++d) acc = fmaf(q[d], sk[j][d], acc);
+      s[j] = (k0 + j < lim) ? acc * a.scale : -INFINITY;
+      mx = fmaxf(mx, s[j]);
+    }
+    const float m_new = fmaxf(m_cur, mx);
+    if (m_new > -INFINITY) {
+      const float alpha = expf(m_cur - m_new);
+      l *= alpha;
+#pragma unroll
+      for (int d = 0; d < DP; ++d) o[d] *= alpha;
+#pragma unroll
+      for (int j = 0; j < TK; ++j) {
+        const float p = expf(s[j] - m_new);
+        l += p;
+#pragma unroll
+        for (int d = 0; d < DP; ++d) o[d] = fmaf(p, sv[j][d], o[d]);
+      }
+      m_cur = m_new;
+    }
+  }
+  if (row_ok) {
+    float* op = reinterpret_cast<float*>(a.o) + b * a.os[0] + (int64_t)qrow * a.os[1] + h * a.os[2];
+    const float inv = 1.0f / l;
+    for (int d = 0; d < a.D; ++d) op[d] = o[d] * inv;
+    if (a.lse != nullptr) a.lse[((int64_t)b * a.H + h) * a.Snew + qrow] = m_cur + logf(l);
+  }
+}
+
+template <int DP>
+hipError_t launch_bf16(const AttnArgs& a, hipStream_t stream) {
+  constexpr int NW = 4;
+  const int n_qtiles = (a.Snew + 32 * NW - 1) / (32 * NW);
+  const long long nblocks = (long long)n_qtiles * a.B * a.H;
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<DP, NW>), dim3((unsigned)nblocks), dim3(NW * 64), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int DP>
+hipError_t launch_f32(const AttnArgs& a, hipStream_t stream) {
+  const int n_qtiles = (a.Snew + 63) / 64;
+  const long long nblocks = (long long)n_qtiles * a.B * a.H;
+  hipLaunchKernelGGL((attn_fwd_f32_kernel<DP>), dim3((unsigned)nblocks), dim3(64), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attention(const AttnArgs& a, int dtype, hipStream_t stream) {
+  const int dp = (a.D + 31) / 32 * 32;
+  if (dtype == 0) {
+    switch (dp) {
+      case 32: return launch_bf16<32>(a, stream);
+      case 64: return launch_bf16<64>(a, stream);
+      case 96: return launch_bf16<96>(a, stream);
+      case 128: return launch_bf16<128>(a, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  switch (dp) {
+    case 32: return launch_f32<32>(a, stream);
+    case 64: return launch_f32<64>(a, stream);
+    case 96: return launch_f32<96>(a, stream);
+    case 128: return launch_f32<128>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace dit

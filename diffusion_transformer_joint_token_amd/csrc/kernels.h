@@ -1,0 +1,64 @@
+// Launch interface between the C-ABI host code and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dit {
+
+constexpr int kMaxImages = 64;
+
+// Token metadata: host-validated image-block shapes and derived constants.
+struct TokenMetaArgs {
+  int32_t seq_len;
+  int32_t n_img;
+  int32_t pos_mode;               // 0 centred (f, h, w); 1 grid (h, w)
+  int32_t max_vid;                // first text position (centred mode)
+  int32_t shape[kMaxImages][3];   // (frames, height, width)
+  int32_t cum[kMaxImages + 1];    // cumulative token counts, cum[0] = 0
+  int32_t frame_off[kMaxImages];  // sum of frames of the earlier blocks
+};
+
+hipError_t launch_token_meta(const uint8_t* mask, const TokenMetaArgs& a, int32_t* image_ids, uint8_t* target,
+                             int32_t* pos, int32_t* kv_limit, int32_t* status, hipStream_t stream);
+
+// Fused QK-RMSNorm + rotary embedding.
+constexpr int kMaxPairs = 64;  // head_dim <= 128
+
+struct QkNormRopeArgs {
+  const void* q;
+  const void* k;
+  void* qo;
+  void* ko;
+  const void* wq;  // nullable: unit weight
+  const void* wk;
+  const int32_t* pos;  // [S][3]
+  int64_t qs[3], ks[3], qos[3], kos[3];
+  int32_t B, S, H, Hk, D;
+  float eps;
+  double omega[kMaxPairs];       // frequency of channel pair p
+  int32_t pair_axis[kMaxPairs];  // axis that owns pair p
+};
+
+hipError_t launch_qknorm_rope(const QkNormRopeArgs& a, int dtype, hipStream_t stream);
+
+// Attention over a (possibly cached) key sequence.  Keys 0..P-1 come from the
+// cache pointers, keys P..P+Snew-1 from the new-token pointers; query row i is
+// logical token P + i.
+struct AttnArgs {
+  const void* q;
+  const void* kc;
+  const void* vc;
+  const void* kn;
+  const void* vn;
+  void* o;
+  float* lse;                // nullable
+  const int32_t* kv_limit;   // logical-sequence bound per token; null for the full mask
+  int64_t qs[3], kcs[3], vcs[3], kns[3], vns[3], os[3];
+  int32_t B, H, Hk, D, P, Snew, Sk;
+  float scale;               // softmax scale
+};
+
+hipError_t launch_attention(const AttnArgs& a, int dtype, hipStream_t stream);
+
+}  // namespace dit

@@ -1,0 +1,188 @@
+// Fused per-head RMSNorm + multi-axis rotary embedding of Q and K (gfx950).
+//
+// NucleusMoE-Image pipeline article, section 6.3: Q and K are RMS-normalised
+// per head (qk_norm = rms_norm) and then rotated by the rotary embedding built
+// over the (frame, height, width) axes (axes_dims_rope (16, 56, 56)).  The
+// Lumina-Next DiT article (configuration table, section 4) gives the 2D split
+// (head_dim / 2 channels per axis, hence head_dim % 4 == 0) and a complex
+// rotary table, i.e. adjacent channel pairs turned by a phase.
+//
+// HBM-bound: each element is read once and written once.  One work-group
+// handles one token (b, s) for all H query heads and H_kv key heads, so the
+// token's rotary phases (one cos/sin per channel pair) are computed once, in
+// double precision before the final fp32 sincos, and shared by every head.
+// A group of LPH lanes owns one head; each lane holds a 16-byte chunk of it
+// (8 bf16 or 4 fp32), so loads and stores are full 16-byte vectors and a
+// head's sum of squares is a butterfly over LPH lanes.
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace dit {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxIter = 4;  // heads per lane-group kept in flight
+
+template <typename T>
+struct Elem;
+template <>
+struct Elem<__bf16> {
+  static constexpr int kPerChunk = 8;
+  __device__ static void unpack(const u32x4& w, float* x) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = bf16_lo(w[i]);
+      x[2 * i + 1] = bf16_hi(w[i]);
+    }
+  }
+  __device__ static u32x4 pack(const float* y) {
+    u32x4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(y[2 * i], y[2 * i + 1]);
+    return w;
+  }
+};
+template <>
+struct Elem<float> {
+  static constexpr int kPerChunk = 4;
+  __device__ static void unpack(const u32x4& w, float* x) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = __builtin_bit_cast(float, static_cast<uint32_t>(w[i]));
+  }
+  __device__ static u32x4 pack(const float* y) {
+    u32x4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = __builtin_bit_cast(uint32_t, y[i]);
+    return w;
+  }
+};
+
+template <typename T, int LPH>
+__global__ __launch_bounds__(kThreads) void qknorm_rope_kernel(QkNormRopeArgs a) {
+  constexpr int EPC = Elem<T>::kPerChunk;  // elements per 16-byte chunk
+  constexpr int SLOTS = kThreads / LPH;    // heads processed side by side
+  __shared__ float2 s_cs[kMaxPairs];
+
+  const int tid = threadIdx.x;
+  const int slot = tid / LPH;
+  const int sub = tid % LPH;
+  const int s = blockIdx.x;
+  const int b = blockIdx.y;
+  const int D = a.D;
+  const int nvh = a.H + a.Hk;
+  const bool lane_active = sub * EPC < D;  // D is a multiple of EPC
+
+  // Per-channel weights for this lane's chunk.
+  float wq[EPC], wk[EPC];
+  {
+    u32x4 raw;
+    if (a.wq != nullptr && lane_active) {
+      raw = *reinterpret_cast<const u32x4*>(reinterpret_cast<const T*>(a.wq) + sub * EPC);
+      Elem<T>::unpack(raw, wq);
+    } else {
+#pragma unroll
+      for (int i = 0; i < EPC; ++i) wq[i] = 1.0f;
+    }
+    if (a.wk != nullptr && lane_active) {
+      raw = *reinterpret_cast<const u32x4*>(reinterpret_cast<const T*>(a.wk) + sub * EPC);
+      Elem<T>::unpack(raw, wk);
+    } else {
+#pragma unroll
+      for (int i = 0; i < EPC; ++i) wk[i] = 1.0f;
+    }
+  }
+
+  bool first = true;
+  for (int vh0 = 0; vh0 < nvh; vh0 += SLOTS * kMaxIter) {
+    // Issue the loads of up to kMaxIter heads before any arithmetic.
+    u32x4 raw[kMaxIter];
+#pragma unroll
+    for (int it = 0; it < kMaxIter; ++it) {
+      const int vh = vh0 + it * SLOTS + slot;
+      raw[it] = u32x4{0, 0, 0, 0};
+      if (vh < nvh && lane_active) {
+        const T* src;
+        if (vh < a.H)
+          src = reinterpret_cast<const T*>(a.q) + b * a.qs[0] + (int64_t)s * a.qs[1] + vh * a.qs[2];
+        else
+          src = reinterpret_cast<const T*>(a.k) + b * a.ks[0] + (int64_t)s * a.ks[1] + (vh - a.H) * a.ks[2];
+        raw[it] = *reinterpret_cast<const u32x4*>(src + sub * EPC);
+      }
+    }
+    if (first) {
+      // Rotary phases of this token, one per channel pair: phase = pos * omega
+      // in double, reduced to [-pi, pi] before the fp32 sincos.
+      if (tid < D / 2) {
+        const int ax = a.pair_axis[tid];
+        const double phase = (double)a.pos[3 * s + ax] * a.omega[tid];
+        const double turns = rint(phase * 0.15915494309189535);  // 1 / (2 pi)
+        const float red = (float)fma(-turns, 6.283185307179586, phase);
+        float sn, cs;
+        sincosf(red, &sn, &cs);
+        s_cs[tid] = make_float2(cs, sn);
+      }
+      __syncthreads();
+      first = false;
+    }
+#pragma unroll
+    for (int it = 0; it < kMaxIter; ++it) {
+      const int vh = vh0 + it * SLOTS + slot;
+      const bool is_q = vh < a.H;
+      float x[EPC];
+      Elem<T>::unpack(raw[it], x);
+      float ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < EPC; ++i) ss = fmaf(x[i], x[i], ss);
+#pragma unroll
+      for (int m = LPH / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+      const float inv = 1.0f / sqrtf(ss / (float)D + a.eps);
+      float y[EPC];
+#pragma unroll
+      for (int i = 0; i < EPC; ++i) y[i] = x[i] * inv * (is_q ? wq[i] : wk[i]);
+#pragma unroll
+      for (int i = 0; i < EPC / 2; ++i) {
+        const float2 cs = s_cs[(sub * EPC) / 2 + i < kMaxPairs ? (sub * EPC) / 2 + i : 0];
+        const float y0 = y[2 * i], y1 = y[2 * i + 1];
+        y[2 * i] = y0 * cs.x - y1 * cs.y;
+        y[2 * i + 1] = y0 * cs.y + y1 * cs.x;
+      }
+      if (vh < nvh && lane_active) {
+        T* dst;
+        if (is_q)
+          dst = reinterpret_cast<T*>(a.qo) + b * a.qos[0] + (int64_t)s * a.qos[1] + vh * a.qos[2];
+        else
+          dst = reinterpret_cast<T*>(a.ko) + b * a.kos[0] + (int64_t)s * a.kos[1] + (vh - a.H) * a.kos[2];
+        *reinterpret_cast<u32x4*>(dst + sub * EPC) = Elem<T>::pack(y);
+      }
+    }
+  }
+}
+
+template <typename T>
+hipError_t launch_typed(const QkNormRopeArgs& a, hipStream_t stream) {
+  constexpr int EPC = Elem<T>::kPerChunk;
+  const int chunks = a.D / EPC;
+  int lph = 1;
+  while (lph < chunks) lph <<= 1;
+  dim3 grid(a.S, a.B);
+  switch (lph) {
+    case 1: hipLaunchKernelGGL((qknorm_rope_kernel<T, 1>), grid, dim3(kThreads), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((qknorm_rope_kernel<T, 2>), grid, dim3(kThreads), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((qknorm_rope_kernel<T, 4>), grid, dim3(kThreads), 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((qknorm_rope_kernel<T, 8>), grid, dim3(kThreads), 0, stream, a); break;
+    case 16: hipLaunchKernelGGL((qknorm_rope_kernel<T, 16>), grid, dim3(kThreads), 0, stream, a); break;
+    case 32: hipLaunchKernelGGL((qknorm_rope_kernel<T, 32>), grid, dim3(kThreads), 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_qknorm_rope(const QkNormRopeArgs& a, int dtype, hipStream_t stream) {
+  return dtype == 0 ? launch_typed<__bf16>(a, stream) : launch_typed<float>(a, stream);
+}
+
+}  // namespace dit

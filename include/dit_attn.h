@@ -1,0 +1,185 @@
+/*
+ * dit_attn.h -- C ABI of the joint text+image DiT attention step on MI355X (gfx950).
+ *
+ * The step is the single-stream attention of a diffusion transformer whose
+ * sequence holds text tokens and image-latent tokens together:
+ *   1. token metadata: per-token image-block ids, target mask, rotary positions
+ *      and the exclusive key bound of each query
+ *      (QwenImage21Transformer2DModel API page, build_token_metadata);
+ *   2. per-head RMSNorm of Q and K, then multi-axis rotary embedding
+ *      (NucleusMoE-Image pipeline article, section 6.3; Lumina-Next DiT article,
+ *      configuration table and section 4);
+ *   3. softmax attention under the full mask or the block-causal rule
+ *      "q_idx >= kv_idx or same image block", with grouped-query heads
+ *      (QwenImage21Transformer2DModel API page, block-causal attention;
+ *      NucleusMoE-Image article, section 6.3);
+ *   4. the same attention with the keys/values of the timestep-independent
+ *      prefix (text and condition images) taken from a cache
+ *      (QwenImage21Transformer2DModel API page, causal_condition and
+ *      forward's kv_cache / kv_cache_mode).
+ *
+ * Conventions shared by every entry point
+ *   - Memory: every pointer marked "device" is device memory owned by the
+ *     caller; "host" pointers are read before the call returns.  The library
+ *     allocates nothing, frees nothing, keeps no state between calls and is
+ *     thread-safe.
+ *   - Layout: activations are [batch, seq, heads, head_dim] ("BSHD") with the
+ *     head_dim axis contiguous; the other three strides are passed in elements
+ *     as {batch, seq, head}.  Base pointers and strides must keep every row
+ *     16-byte aligned.
+ *   - Streams: `stream` is a hipStream_t (NULL = the default stream).  All work
+ *     is enqueued asynchronously; no call synchronises.
+ *   - Empty work: a qknorm/attention call with B == 0 or S == 0 (S_new == 0)
+ *     returns DIT_ATTN_OK at once and reads none of its pointers.
+ *   - Errors: argument errors are found on the host before anything is
+ *     enqueued and returned as a dit_attn_status; a failed launch returns
+ *     DIT_ATTN_ERR_HIP.  Errors that depend on device data (see
+ *     dit_attn_build_token_metadata) are written to a device status word.
+ *     Nothing aborts and no exception crosses the ABI.
+ */
+#ifndef DIT_ATTN_H
+#define DIT_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DIT_ATTN_OK = 0,
+  DIT_ATTN_ERR_NULL = 1,        /* a required pointer is NULL */
+  DIT_ATTN_ERR_SHAPE = 2,       /* sizes inconsistent or out of range */
+  DIT_ATTN_ERR_UNSUPPORTED = 3, /* valid request this build does not implement */
+  DIT_ATTN_ERR_ALIGN = 4,       /* pointer or stride breaks 16-byte row alignment */
+  DIT_ATTN_ERR_DATA = 5,        /* device data break the layout contract (status word) */
+  DIT_ATTN_ERR_HIP = 6          /* a HIP runtime call or launch failed */
+} dit_attn_status;
+
+typedef enum { DIT_ATTN_BF16 = 0, DIT_ATTN_F32 = 1 } dit_attn_dtype;
+
+typedef enum {
+  DIT_ATTN_MASK_FULL = 0,        /* every query sees every key */
+  DIT_ATTN_MASK_BLOCK_CAUSAL = 1 /* q sees k iff k <= q or both in one image block */
+} dit_attn_mask_mode;
+
+typedef enum {
+  /* 3 axes (frame, height, width).  Image token (f, h, w) of a block of shape
+   * (F, H, W) sits at (frame offset of the block + f, h - H/2, w - W/2); the
+   * frame offset is the sum of F over earlier blocks.  Text token number t
+   * (counting text tokens in sequence order) sits at max_vid_index + t on all
+   * three axes, max_vid_index being one past the largest image coordinate
+   * (0 with no image).  H and W must be even. */
+  DIT_ATTN_POS_CENTERED_FHW = 0,
+  /* 2 axes (height, width) from 0 inside each single-frame block; third
+   * column 0.  Image tokens only (a text token is a data error). */
+  DIT_ATTN_POS_GRID_HW = 1
+} dit_attn_pos_mode;
+
+/* Largest number of image blocks per sequence. */
+#define DIT_ATTN_MAX_IMAGES 64
+
+/* Token metadata of one joint sequence (shared by every batch element: all
+ * samples share the layout, QwenImage21Transformer2DModel API page, forward's
+ * img_shapes).  The struct is a host object; its pointers are device buffers
+ * the caller owns, each with seq_len entries (pos_ids: seq_len * 3). */
+typedef struct {
+  int32_t *image_ids;   /* [seq_len] text = -1, image block b = b (0-based)       */
+  uint8_t *target_mask; /* [seq_len] 1 on tokens of the last (target) image block */
+  int32_t *pos_ids;     /* [seq_len][3] rotary positions (see dit_attn_pos_mode)  */
+  int32_t *kv_limit;    /* [seq_len] exclusive bound of the keys token s may see
+                           under the block-causal rule: s + 1 for text, one past
+                           the last token of its block for image tokens          */
+  int32_t seq_len;
+} dit_attn_token_meta;
+
+/* Token metadata (QwenImage21Transformer2DModel API page, build_token_metadata).
+ *   image_pad_mask  device uint8 [seq_len], nonzero on image tokens.
+ *   img_shapes      host int32 [n_img][3] = (frames, height, width) of each image
+ *                   block in sequence order, condition images first, the target
+ *                   last.  Block boundaries follow these token counts, not runs of
+ *                   nonzero mask entries: adjacent images stay separate blocks.
+ *   n_img           0..DIT_ATTN_MAX_IMAGES (0 = text only; nothing is target).
+ *   pos_mode        dit_attn_pos_mode.
+ *   meta            host struct of caller-owned device output buffers;
+ *                   meta->seq_len must equal seq_len.
+ *   status_dev      device int32 [1]; receives DIT_ATTN_OK or DIT_ATTN_ERR_DATA when
+ *                   the mask marks a different number of tokens than img_shapes
+ *                   describe, a block's tokens are not contiguous, or (GRID_HW) a
+ *                   text token is present.  On a data error the outputs are
+ *                   unspecified.  Read it after the stream has run the call.
+ * Host-side errors: NULL pointers, seq_len < 1, n_img out of range, an extent < 1,
+ * odd H/W (CENTERED_FHW), frames != 1 (GRID_HW), unknown pos_mode. */
+int dit_attn_build_token_metadata(const uint8_t *image_pad_mask, int32_t seq_len,
+                                  const int32_t *img_shapes, int32_t n_img, int32_t pos_mode,
+                                  const dit_attn_token_meta *meta, int32_t *status_dev,
+                                  void *stream);
+
+/* Fused per-head RMSNorm + multi-axis rotary embedding of Q and K
+ * (NucleusMoE-Image pipeline article, section 6.3: qk_norm then rotary;
+ *  Lumina-Next DiT article: 2D rotary needs head_dim % 4 == 0).
+ * For every (b, s, head) of Q (H heads) and K (H_kv heads):
+ *   y = x / sqrt(mean_d x_d^2 + eps) * w            (w: q_weight or k_weight)
+ *   then for axis a owning channels [o_a, o_a + d_a), pair j turns
+ *   (y[o_a+2j], y[o_a+2j+1]) by pos[s][a] * rope_theta^(-2j/d_a).
+ * V is not touched.  Arithmetic in fp32; outputs rounded to the dtype (RNE).
+ *   q, k           device [B, S, H | H_kv, D] in dtype, strides q_strides/k_strides.
+ *   q_out, k_out   device outputs (may alias q, k exactly), strides qo_/ko_strides.
+ *   q_weight, k_weight  device [D] in dtype, or NULL for unit weights.
+ *   pos_ids        device int32 [S][3] (the metadata's pos_ids; for the new
+ *                  tokens of a cached step pass meta.pos_ids + 3 * prefix_len).
+ *   n_axes         2 or 3; axes_dims host int32 [n_axes], each even, summing to D.
+ *   rope_theta     rotary base (> 0).  eps >= 0.
+ * Requirements: D % 8 == 0 (bf16) or D % 4 == 0 (f32), 8 <= D <= 128. */
+int dit_attn_qknorm_rope(const void *q, const void *k, void *q_out, void *k_out,
+                         const void *q_weight, const void *k_weight,
+                         int32_t B, int32_t S, int32_t H, int32_t H_kv, int32_t D,
+                         const int64_t q_strides[3], const int64_t k_strides[3],
+                         const int64_t qo_strides[3], const int64_t ko_strides[3],
+                         const int32_t *pos_ids, int32_t n_axes, const int32_t *axes_dims,
+                         float rope_theta, float eps, int32_t dtype, void *stream);
+
+/* Masked softmax attention (QwenImage21Transformer2DModel API page, block-causal
+ * attention; NucleusMoE-Image article section 6.3 for GQA):
+ *   O[b,q,h] = sum_k softmax_k(scale * <Q[b,q,h], K[b,k,g]>) V[b,k,g],  g = h / (H/H_kv)
+ * over the keys k allowed for q: all keys (FULL) or k < meta->kv_limit[q]
+ * (BLOCK_CAUSAL; this prefix is exactly "k <= q or same image block" for
+ * contiguous blocks).
+ *   q, k, v, o   device [B, S, H|H_kv|H_kv|H, D]; strides[0..3] = q, k, v, o.
+ *   lse          device float [B, H, S] natural-log sum-exp of the scaled logits,
+ *                or NULL.
+ *   meta         host struct; only kv_limit is read (may be NULL for FULL);
+ *                meta->seq_len must equal S.
+ *   softmax_scale  <= 0 selects 1/sqrt(D).
+ * bf16: QK^T and PV on bf16 MFMA with fp32 accumulation, P rounded to bf16 for
+ * PV, O rounded once.  f32: fp32 throughout.  D <= 128, D % 8 == 0. */
+int dit_attn_forward(const void *q, const void *k, const void *v, void *o, float *lse,
+                     int32_t B, int32_t S, int32_t H, int32_t H_kv, int32_t D,
+                     const int64_t strides[4][3], int32_t mask_mode,
+                     const dit_attn_token_meta *meta, float softmax_scale, int32_t dtype,
+                     void *stream);
+
+/* Attention of the new tokens of a cached step (QwenImage21Transformer2DModel API
+ * page, kv_cache_mode "cached"): the logical sequence has P prefix tokens whose
+ * keys/values come from the cache, followed by S_new new tokens.  Query row i is
+ * logical token P + i; keys 0..P-1 are read from k_cache/v_cache (post-norm,
+ * post-rotary K; raw V) and keys P..P+S_new-1 from k_new/v_new.  The mask and
+ * everything else are those of dit_attn_forward on the logical sequence, so the
+ * rows equal rows P.. of a full forward over cache+new.
+ *   strides[0..5] = q_new, k_cache, v_cache, k_new, v_new, o.
+ *   meta->seq_len must equal P + S_new; P >= 0 (P == 0 is a plain forward). */
+int dit_attn_forward_cached(const void *q_new, const void *k_cache, const void *v_cache,
+                            const void *k_new, const void *v_new, void *o, float *lse,
+                            int32_t B, int32_t P, int32_t S_new, int32_t H, int32_t H_kv,
+                            int32_t D, const int64_t strides[6][3], int32_t mask_mode,
+                            const dit_attn_token_meta *meta, float softmax_scale,
+                            int32_t dtype, void *stream);
+
+/* Static description of a status code (never NULL). */
+const char *dit_attn_status_string(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DIT_ATTN_H */

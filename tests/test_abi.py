@@ -1,0 +1,128 @@
+"""The C-ABI library loads, exports what include/dit_attn.h declares, and
+rejects bad arguments on the host before touching a device (CPU only: every
+call here fails validation, so nothing is enqueued)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dit_attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*(dit_attn_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    from diffusion_transformer_joint_token_amd import _lib
+    names = declared_functions()
+    assert names == sorted(_lib.EXPORTED)
+    for name in names:
+        assert hasattr(_lib.lib, name), name
+    out = os.popen("nm -D --defined-only %s" % _lib.LIB_PATH).read()
+    for name in names:
+        assert re.search(r"\bT %s$" % name, out, re.M), name
+
+
+def test_status_strings():
+    from diffusion_transformer_joint_token_amd import _lib
+    for code in range(7):
+        assert _lib.lib.dit_attn_status_string(code)
+    assert _lib.lib.dit_attn_status_string(99) == b"unknown status"
+
+
+FAKE = 0x100000  # 16-byte aligned, never dereferenced: validation fails first
+FAKE2 = 0x200000
+
+
+def _meta(seq_len, ptr=FAKE):
+    from diffusion_transformer_joint_token_amd import _lib
+    return _lib.TokenMetaStruct(ptr, ptr, ptr, ptr, seq_len)
+
+
+def test_metadata_argument_errors():
+    from diffusion_transformer_joint_token_amd import _lib
+    lib = _lib.lib
+    m = _meta(16)
+    shapes = (ctypes.c_int32 * 3)(1, 4, 4)
+    f = lib.dit_attn_build_token_metadata
+    assert f(None, 16, shapes, 1, 0, ctypes.byref(m), FAKE, None) == _lib.ERR_NULL
+    assert f(FAKE, 16, shapes, 1, 0, None, FAKE, None) == _lib.ERR_NULL
+    assert f(FAKE, 16, shapes, 1, 0, ctypes.byref(m), None, None) == _lib.ERR_NULL
+    assert f(FAKE, 17, shapes, 1, 0, ctypes.byref(m), FAKE, None) == _lib.ERR_SHAPE       # seq_len mismatch
+    assert f(FAKE, 16, shapes, 65, 0, ctypes.byref(m), FAKE, None) == _lib.ERR_SHAPE      # too many images
+    assert f(FAKE, 16, shapes, 1, 7, ctypes.byref(m), FAKE, None) == _lib.ERR_UNSUPPORTED  # pos mode
+    odd = (ctypes.c_int32 * 3)(1, 3, 4)
+    assert f(FAKE, 16, odd, 1, 0, ctypes.byref(m), FAKE, None) == _lib.ERR_SHAPE          # odd H, centred
+    frames = (ctypes.c_int32 * 3)(2, 2, 2)
+    assert f(FAKE, 16, frames, 1, 1, ctypes.byref(m), FAKE, None) == _lib.ERR_SHAPE       # 2 frames, 2D grid
+    big = (ctypes.c_int32 * 6)(1, 4, 4, 1, 2, 2)
+    assert f(FAKE, 16, big, 2, 0, ctypes.byref(m), FAKE, None) == _lib.ERR_SHAPE          # 20 image tokens > 16
+    zero = (ctypes.c_int32 * 3)(1, 0, 4)
+    assert f(FAKE, 16, zero, 1, 0, ctypes.byref(m), FAKE, None) == _lib.ERR_SHAPE
+
+
+def _s3(*v):
+    from diffusion_transformer_joint_token_amd import _lib
+    return _lib.Strides3(*v)
+
+
+def test_qknorm_rope_argument_errors():
+    from diffusion_transformer_joint_token_amd import _lib
+    f = _lib.lib.dit_attn_qknorm_rope
+    st = _s3(5120 * 4096, 4096, 128)
+    axes = (ctypes.c_int32 * 3)(16, 56, 56)
+
+    def call(q=FAKE, D=128, axes_arr=axes, n_axes=3, dtype=0, strides=st, theta=1e4, eps=1e-6, H=32, Hk=32):
+        return f(q, FAKE, FAKE2, FAKE2, None, None, 2, 5120, H, Hk, D, strides, strides, strides, strides, FAKE,
+                 n_axes, axes_arr, theta, eps, dtype, None)
+    assert call(q=None) == _lib.ERR_NULL
+    assert call(dtype=5) == _lib.ERR_UNSUPPORTED
+    assert call(D=136) == _lib.ERR_UNSUPPORTED
+    assert call(D=100) == _lib.ERR_UNSUPPORTED           # not a multiple of 8 (bf16)
+    assert call(axes_arr=(ctypes.c_int32 * 3)(16, 56, 54)) == _lib.ERR_SHAPE   # sums to 126
+    assert call(axes_arr=(ctypes.c_int32 * 3)(15, 57, 56)) == _lib.ERR_SHAPE   # odd axis
+    assert call(n_axes=4) == _lib.ERR_SHAPE
+    assert call(theta=0.0) == _lib.ERR_SHAPE
+    assert call(eps=-1.0) == _lib.ERR_SHAPE
+    assert call(H=0) == _lib.ERR_SHAPE
+    assert call(q=FAKE + 2) == _lib.ERR_ALIGN
+    assert call(strides=_s3(5120 * 4096, 4096, 132)) == _lib.ERR_ALIGN   # head stride 264 B
+
+
+def test_attention_argument_errors():
+    from diffusion_transformer_joint_token_amd import _lib
+    f = _lib.lib.dit_attn_forward
+    st4 = (_lib.Strides3 * 4)(*[_s3(5120 * 4096, 4096, 128)] * 4)
+    m = _meta(5120)
+
+    def call(q=FAKE, S=5120, H=32, Hk=32, D=128, mask=1, meta=m, dtype=0, strides=st4):
+        return f(q, FAKE, FAKE, FAKE2, None, 2, S, H, Hk, D, strides, mask,
+                 ctypes.byref(meta) if meta is not None else None, 0.0, dtype, None)
+    assert call(q=None) == _lib.ERR_NULL
+    assert call(meta=None) == _lib.ERR_NULL                 # block-causal needs kv_limit
+    assert call(S=5000) == _lib.ERR_SHAPE                   # metadata length mismatch
+    assert call(Hk=5) == _lib.ERR_SHAPE                     # 32 % 5
+    assert call(D=256) == _lib.ERR_UNSUPPORTED
+    assert call(mask=3) == _lib.ERR_UNSUPPORTED
+    assert call(dtype=2) == _lib.ERR_UNSUPPORTED
+    assert call(q=FAKE + 8) == _lib.ERR_ALIGN
+    fc = _lib.lib.dit_attn_forward_cached
+    st6 = (_lib.Strides3 * 6)(*[_s3(5120 * 4096, 4096, 128)] * 6)
+    assert fc(FAKE, None, None, FAKE, FAKE, FAKE2, None, 1, 16, 100, 32, 32, 128, st6, 1, ctypes.byref(_meta(116)),
+              0.0, 0, None) == _lib.ERR_NULL            # P > 0 needs the cache
+    assert fc(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE2, None, 1, 16, 100, 32, 32, 128, st6, 1,
+              ctypes.byref(_meta(100)), 0.0, 0, None) == _lib.ERR_SHAPE   # seq_len must be P + S_new
+
+
+def test_empty_inputs_are_noops():
+    """B == 0 or S == 0 returns OK without launching anything."""
+    from diffusion_transformer_joint_token_amd import _lib
+    st4 = (_lib.Strides3 * 4)(*[_s3(0, 4096, 128)] * 4)
+    assert _lib.lib.dit_attn_forward(FAKE, FAKE, FAKE, FAKE2, None, 0, 16, 32, 32, 128, st4, 0, None, 0.0, 0,
+                                     None) == _lib.OK
+    assert _lib.lib.dit_attn_forward(FAKE, FAKE, FAKE, FAKE2, None, 2, 0, 32, 32, 128, st4, 0, None, 0.0, 0,
+                                     None) == _lib.OK

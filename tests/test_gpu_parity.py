@@ -1,0 +1,361 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Every input is drawn by the seeded generator in ``workloads`` and handed to
+both sides; no expected value comes from the GPU.  Small cases compare every
+output element and span several query tiles (128 rows), key tiles (64 keys)
+and a ragged tail; the five full-size workloads compare sampled query rows the
+oracle computes one by one, at the same launch configuration the benchmark
+times.
+"""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.attention as oatt
+import oracle.metadata as ometa
+import oracle.qknorm_rope as oqr
+import workloads as wl
+from tests.gpu_helpers import assert_parity, to_device, to_host
+
+pytestmark = pytest.mark.gpu
+
+GPU_OK = torch.cuda.is_available()
+
+
+@pytest.fixture(scope="module")
+def dit():
+    if not GPU_OK:
+        pytest.fail("no GPU visible: the gpu-marked tests need an MI355X")
+    import diffusion_transformer_joint_token_amd as d
+    return d
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+# --------------------------------------------------------------------------- helpers
+def _meta_gpu(dit, mask: np.ndarray, shapes, pos_mode):
+    m = dit.build_token_metadata(torch.from_numpy(mask).cuda(), shapes, pos_mode)
+    m.check()
+    return m
+
+
+def _axes3(axes):
+    return list(axes)
+
+
+def sample_rows(w: wl.Workload, n_random=24, seed=0):
+    """First/last rows, rows around every segment boundary, and random rows
+    (indices into the query tokens)."""
+    S = w.n_new
+    rows = {0, 1, 2, 3, S - 1, S - 2, S - 3}
+    start = 0
+    for seg in w.layout:
+        n = seg[1] if seg[0] == "T" else seg[1] * seg[2] * seg[3]
+        for r in (start - 1, start, start + 1, start + n - 1):
+            q = r - w.prefix_len
+            if 0 <= q < S:
+                rows.add(q)
+        start += n
+    rng = np.random.default_rng(seed)
+    rows.update(int(x) for x in rng.integers(0, S, size=n_random))
+    return np.array(sorted(rows))
+
+
+# --------------------------------------------------------------------------- token metadata
+LAYOUTS = {name: w.layout for name, w in wl.WORKLOADS.items()}
+
+
+@pytest.mark.parametrize("name", list(wl.WORKLOADS))
+def test_metadata_workloads_bit_exact(dit, name):
+    w = wl.WORKLOADS[name]
+    _say("metadata %s" % name)
+    mask, shapes = wl.sequence_inputs(w)
+    m = _meta_gpu(dit, mask, shapes, w.pos_mode)
+    ref = ometa.build_token_metadata(mask, shapes, w.pos_mode)
+    for key in ("image_ids", "target_mask", "pos_ids", "kv_limit"):
+        got = getattr(m, key).cpu().numpy()
+        assert np.array_equal(got, ref[key].astype(got.dtype)), key
+
+
+def test_metadata_goldens_and_random_layouts(dit):
+    from tests import goldens
+    from tests.oracle_pins import random_layout
+    cases = []
+    for name in goldens.metadata_fixtures():
+        g = goldens.load(name)
+        cases.append((g["layout"], g["pos_mode"]))
+    rng = np.random.default_rng(21)
+    for i in range(20):
+        cases.append((random_layout(rng, 60), "centered_fhw"))
+    for i in range(10):
+        # longer sequences (several 1024-token chunks of the scan), <= 64 blocks
+        segs, n = [], 0
+        while n < 3000 and len(segs) < 100:
+            if rng.random() < 0.4:
+                t = int(rng.integers(1, 300))
+                segs.append(("T", t))
+            else:
+                f, hh, ww = int(rng.integers(1, 3)), 2 * int(rng.integers(1, 9)), 2 * int(rng.integers(1, 9))
+                segs.append(("I", f, hh, ww))
+                t = f * hh * ww
+            n += t
+        cases.append((tuple(segs), "centered_fhw"))
+    cases.append(((("T", 1),), "centered_fhw"))
+    cases.append(((("I", 1, 2, 2), ("I", 1, 4, 6), ("I", 1, 2, 2)), "grid_hw"))
+    for layout, mode in cases:
+        w = wl.small_workload("m", 1, 1, 1, 8, layout, (8,), pos_mode=mode)
+        mask, shapes = wl.sequence_inputs(w)
+        m = _meta_gpu(dit, mask, shapes, mode)
+        ref = ometa.build_token_metadata(mask, shapes, mode)
+        for key in ("image_ids", "target_mask", "pos_ids", "kv_limit"):
+            got = getattr(m, key).cpu().numpy()
+            assert np.array_equal(got, ref[key].astype(got.dtype)), (layout, key)
+
+
+def test_metadata_data_errors(dit):
+    def status(mask, shapes, mode="centered_fhw"):
+        m = dit.build_token_metadata(torch.tensor(mask, dtype=torch.uint8).cuda(), shapes, mode)
+        torch.cuda.synchronize()
+        return int(m.status.item())
+    assert status([1, 1, 1, 1], [(1, 2, 2)]) == 0
+    assert status([1, 1, 1, 0], [(1, 2, 2)]) == 5          # too few image tokens
+    assert status([1, 1, 1, 1, 1, 0], [(1, 2, 2)]) == 5    # too many
+    assert status([1, 1, 0, 1, 1], [(1, 2, 2)]) == 5       # block split by text
+    assert status([0, 1, 1], [(1, 1, 2)], "grid_hw") == 5  # text under 2D positions
+    with pytest.raises(dit.DitAttnError):
+        dit.build_token_metadata(torch.ones(6, dtype=torch.uint8).cuda(), [(1, 3, 2)])  # odd H, centred
+
+
+# --------------------------------------------------------------------------- qk-norm + rope
+NORM_CASES = [
+    # (B, S, H, Hk, D, axes, dtype, unit_weights, pos layout)
+    (1, 32, 2, 2, 32, (4, 14, 14), "f32", True, (("T", 16), ("I", 1, 4, 4))),
+    (2, 50, 3, 1, 8, (4, 4), "bf16", False, (("I", 1, 5, 10),)),
+    (1, 37, 4, 2, 16, (8, 4, 4), "bf16", False, (("T", 5), ("I", 1, 4, 8))),
+    (2, 300, 8, 2, 72, (36, 36), "bf16", False, (("I", 1, 15, 20),)),
+    (1, 200, 6, 6, 128, (16, 56, 56), "bf16", False, (("T", 72), ("I", 2, 8, 8))),
+    (2, 90, 4, 4, 64, (16, 24, 24), "f32", False, (("T", 10), ("I", 1, 8, 10))),
+    (1, 40, 2, 1, 128, (16, 56, 56), "f32", False, (("T", 8), ("I", 2, 4, 4))),
+]
+
+
+@pytest.mark.parametrize("case", NORM_CASES, ids=lambda c: "B%dS%dH%d_%dD%d_%s" % (c[0], c[1], c[2], c[3], c[4], c[6]))
+def test_qknorm_rope_small(dit, case):
+    B, S, H, Hk, D, axes, dtype, unit, layout = case
+    mode = "grid_hw" if len(axes) == 2 else "centered_fhw"
+    w = wl.small_workload("n", B, H, Hk, D, layout, axes, pos_mode=mode, dtype=dtype, unit_weights=unit, seed=S)
+    assert w.seq_len == S
+    _say("qknorm_rope %s" % (case,))
+    d = wl.draw(w)
+    mask, shapes = wl.sequence_inputs(w)
+    md = ometa.build_token_metadata(mask, shapes, mode)
+    m = _meta_gpu(dit, mask, shapes, mode)
+    q, k = to_device(d.bits["q"], dtype), to_device(d.bits["k"], dtype)
+    wq, wk = to_device(d.bits["wq"], dtype), to_device(d.bits["wk"], dtype)
+    qo, ko = dit.qknorm_rope(q, k, m.pos_ids, axes, w.eps, wq, wk)
+    torch.cuda.synchronize()
+    rq = oqr.qknorm_rope(d.vals["q"], d.vals["wq"], w.eps, md["pos_ids"], axes)
+    rk = oqr.qknorm_rope(d.vals["k"], d.vals["wk"], w.eps, md["pos_ids"], axes)
+    assert_parity(to_host(qo), rq, dtype, "q'")
+    assert_parity(to_host(ko), rk, dtype, "k'")
+    # In place on strided views of one fused buffer gives the same bits.
+    fused = torch.zeros(B, S, H + 2 * Hk + 1, D, dtype=q.dtype, device="cuda")
+    fused[:, :, :H] = q
+    fused[:, :, H:H + Hk] = k
+    qv, kv = fused[:, :, :H], fused[:, :, H:H + Hk]
+    dit.qknorm_rope(qv, kv, m.pos_ids, axes, w.eps, wq, wk, inplace=True)
+    torch.cuda.synchronize()
+    assert torch.equal(qv, qo) and torch.equal(kv, ko)
+
+
+@pytest.mark.parametrize("name", list(wl.WORKLOADS))
+def test_qknorm_rope_workloads_sampled(dit, name):
+    w = wl.WORKLOADS[name]
+    _say("qknorm_rope full %s" % name)
+    d = wl.draw(w, parts=("q", "k", "wq", "wk"))
+    mask, shapes = wl.sequence_inputs(w)
+    md = ometa.build_token_metadata(mask, shapes, w.pos_mode)
+    m = _meta_gpu(dit, mask, shapes, w.pos_mode)
+    P = w.prefix_len
+    q, k = to_device(d.bits["q"], w.dtype), to_device(d.bits["k"], w.dtype)
+    wq, wk = to_device(d.bits["wq"], w.dtype), to_device(d.bits["wk"], w.dtype)
+    qo, ko = dit.qknorm_rope(q, k, m.pos_ids[P:], w.axes, w.eps, wq, wk)
+    torch.cuda.synchronize()
+    rows = sample_rows(w, 64)
+    pos = md["pos_ids"][P:][rows]
+    rq = oqr.qknorm_rope(d.vals["q"][:, rows], d.vals["wq"], w.eps, pos, w.axes)
+    rk = oqr.qknorm_rope(d.vals["k"][:, rows], d.vals["wk"], w.eps, pos, w.axes)
+    idx = torch.from_numpy(rows).cuda()
+    assert_parity(to_host(qo[:, idx]), rq, w.dtype, "q'")
+    assert_parity(to_host(ko[:, idx]), rk, w.dtype, "k'")
+
+
+# --------------------------------------------------------------------------- attention
+ATT_CASES = [
+    # (B, H, Hk, D, layout, mask_mode, dtype, prefix)
+    (1, 2, 2, 32, (("T", 16), ("I", 1, 4, 4)), "block_causal", "f32", 0),
+    (2, 4, 2, 128, (("T", 100), ("I", 1, 6, 10), ("T", 37), ("I", 1, 4, 8)), "block_causal", "bf16", 0),
+    (2, 4, 2, 128, (("T", 100), ("I", 1, 6, 10), ("T", 37), ("I", 1, 4, 8)), "full", "bf16", 0),
+    (1, 6, 3, 72, (("I", 1, 14, 22),), "full", "bf16", 0),
+    (1, 3, 1, 8, (("I", 1, 4, 4),), "full", "bf16", 0),
+    (2, 2, 1, 16, (("T", 5), ("I", 1, 2, 4), ("T", 70), ("I", 1, 8, 8)), "block_causal", "bf16", 0),
+    (1, 4, 4, 64, (("T", 256), ("I", 1, 8, 8), ("I", 1, 8, 8), ("T", 30), ("I", 1, 10, 16)), "block_causal",
+     "bf16", 0),
+    (1, 4, 2, 128, (("T", 130), ("I", 1, 4, 8), ("I", 1, 10, 20)), "block_causal", "bf16", 162),
+    (1, 2, 2, 128, (("T", 64), ("I", 1, 8, 8), ("I", 1, 16, 16)), "block_causal", "bf16", 128),
+    (1, 2, 2, 96, (("T", 40), ("I", 1, 6, 6), ("T", 9)), "block_causal", "f32", 17),
+    (1, 1, 1, 128, (("T", 1),), "block_causal", "bf16", 0),
+]
+
+
+def _case_id(c):
+    return "B%dH%d_%dD%d_%s_%s_S%dP%d" % (c[0], c[1], c[2], c[3], c[5], c[6], sum(
+        s[1] if s[0] == "T" else s[1] * s[2] * s[3] for s in c[4]), c[7])
+
+
+@pytest.mark.parametrize("case", ATT_CASES, ids=_case_id)
+def test_attention_small_all_rows(dit, case):
+    """Synthetic Q', K', V straight into the attention entry points (no norm),
+    every output element and the lse checked."""
+    B, H, Hk, D, layout, mode, dtype, P = case
+    w = wl.small_workload("a", B, H, Hk, D, layout, (D,), dtype=dtype, seed=D + P, prefix_len=P)
+    _say("attention %s" % _case_id(case))
+    d = wl.draw(w)
+    mask, shapes = wl.sequence_inputs(w)
+    md = ometa.build_token_metadata(mask, shapes)
+    m = _meta_gpu(dit, mask, shapes, "centered_fhw")
+    q, k, v = (to_device(d.bits[n], dtype) for n in ("q", "k", "v"))
+    if P:
+        kc, vc = to_device(d.bits["k_cache"], dtype), to_device(d.bits["v_cache"], dtype)
+        o, lse = dit.forward_cached(q, kc, vc, k, v, mode, m, return_lse=True)
+        k_all = np.concatenate([d.vals["k_cache"], d.vals["k"]], axis=1)
+        v_all = np.concatenate([d.vals["v_cache"], d.vals["v"]], axis=1)
+    else:
+        o, lse = dit.forward(q, k, v, mode, m, return_lse=True)
+        k_all, v_all = d.vals["k"], d.vals["v"]
+    torch.cuda.synchronize()
+    ro, rl = oatt.attention(d.vals["q"], k_all, v_all, md["image_ids"], mode, q_offset=P)
+    assert_parity(to_host(o), ro, dtype, "O")
+    assert_parity(lse.cpu().double().numpy(), rl, "f32", "lse", atol=1e-2 if dtype == "bf16" else 1e-5)
+
+
+def _pipeline(dit, w: wl.Workload, d: wl.Drawn, m):
+    """K2 then K3 on the GPU for workload w; returns (o, lse, q', k')."""
+    P = w.prefix_len
+    q, k, v = (to_device(d.bits[n], w.dtype) for n in ("q", "k", "v"))
+    wq, wk = to_device(d.bits["wq"], w.dtype), to_device(d.bits["wk"], w.dtype)
+    qp, kp = dit.qknorm_rope(q, k, m.pos_ids[P:], w.axes, w.eps, wq, wk)
+    if P:
+        kc, vc = to_device(d.bits["k_cache"], w.dtype), to_device(d.bits["v_cache"], w.dtype)
+        o, lse = dit.forward_cached(qp, kc, vc, kp, v, w.mask_mode, m, return_lse=True)
+    else:
+        o, lse = dit.forward(qp, kp, v, w.mask_mode, m, return_lse=True)
+    torch.cuda.synchronize()
+    return o, lse, qp, kp
+
+
+@pytest.mark.parametrize("name", list(wl.WORKLOADS))
+def test_pipeline_workloads(dit, name):
+    """The whole step (metadata -> norm+rope -> attention) at full size; the
+    oracle computes sampled query rows (all rows for the tiny workload)."""
+    w = wl.WORKLOADS[name]
+    _say("pipeline %s" % name)
+    d = wl.draw(w)
+    mask, shapes = wl.sequence_inputs(w)
+    md = ometa.build_token_metadata(mask, shapes, w.pos_mode)
+    m = _meta_gpu(dit, mask, shapes, w.pos_mode)
+    o, lse, _, _ = _pipeline(dit, w, d, m)
+    P = w.prefix_len
+    rows = np.arange(w.n_new) if w.n_new <= 64 else sample_rows(w)
+    pos = md["pos_ids"][P:]
+    qp = oqr.qknorm_rope(d.vals["q"][:, rows], d.vals["wq"], w.eps, pos[rows], w.axes)
+    kp = oqr.qknorm_rope(d.vals["k"], d.vals["wk"], w.eps, pos, w.axes)
+    k_all = np.concatenate([d.vals["k_cache"], kp], axis=1) if P else kp
+    v_all = np.concatenate([d.vals["v_cache"], d.vals["v"]], axis=1) if P else d.vals["v"]
+    # query token r sits at logical position P + r
+    ro = np.zeros((w.batch, rows.size, w.heads, w.head_dim))
+    rl = np.zeros((w.batch, w.heads, rows.size))
+    for j, r in enumerate(rows):
+        oj, lj = oatt.attention(qp[:, j:j + 1], k_all, v_all, md["image_ids"], w.mask_mode, q_offset=P + int(r))
+        ro[:, j] = oj[:, 0]
+        rl[:, :, j] = lj[:, :, 0]
+    idx = torch.from_numpy(rows).cuda()
+    stats = assert_parity(to_host(o[:, idx]), ro, w.dtype, "O")
+    assert_parity(lse[:, :, idx].cpu().double().numpy(), rl, "f32", "lse", atol=1e-2 if w.dtype == "bf16" else 1e-5)
+    _say("  %s rows=%d max=%.3g mean=%.3g" % (name, rows.size, stats["max"], stats["mean"]))
+
+
+# --------------------------------------------------------------------------- invariants on device outputs
+def test_cached_rows_equal_full_rows(dit):
+    """forward_cached over (cache = rows [0, P) of K', V) equals rows P.. of the
+    full forward; prefix rows do not change when the target's K/V change."""
+    layout = (("T", 200), ("I", 1, 8, 8), ("I", 1, 12, 16))
+    w = wl.small_workload("c", 1, 4, 2, 128, layout, (16, 56, 56), seed=77)
+    d = wl.draw(w)
+    mask, shapes = wl.sequence_inputs(w)
+    m = _meta_gpu(dit, mask, shapes, "centered_fhw")
+    q, k, v = (to_device(d.bits[n], "bf16") for n in ("q", "k", "v"))
+    P = 264
+    full = dit.forward(q, k, v, "block_causal", m)
+    cached = dit.forward_cached(q[:, P:].contiguous(), k[:, :P].contiguous(), v[:, :P].contiguous(),
+                                k[:, P:].contiguous(), v[:, P:].contiguous(), "block_causal", m)
+    torch.cuda.synchronize()
+    # Each row's result depends only on its own keys and the fixed key tiling,
+    # so the cached rows are bit-identical to the full forward's rows.
+    assert torch.equal(cached, full[:, P:])
+    k2, v2 = k.clone(), v.clone()
+    k2[:, P:] = torch.randn_like(k2[:, P:])
+    v2[:, P:] = torch.randn_like(v2[:, P:])
+    full2 = dit.forward(q, k2, v2, "block_causal", m)
+    torch.cuda.synchronize()
+    assert torch.equal(full2[:, :P], full[:, :P])
+
+
+def test_gqa_equals_expanded_heads(dit):
+    layout = (("T", 90), ("I", 1, 10, 12))
+    w = wl.small_workload("g", 2, 8, 2, 72, layout, (72,), seed=5)
+    d = wl.draw(w)
+    mask, shapes = wl.sequence_inputs(w)
+    m = _meta_gpu(dit, mask, shapes, "centered_fhw")
+    q, k, v = (to_device(d.bits[n], "bf16") for n in ("q", "k", "v"))
+    o = dit.forward(q, k, v, "block_causal", m)
+    ke = torch.repeat_interleave(k, 4, dim=2).contiguous()
+    ve = torch.repeat_interleave(v, 4, dim=2).contiguous()
+    oe = dit.forward(q, ke, ve, "block_causal", m)
+    torch.cuda.synchronize()
+    assert torch.equal(o, oe)
+
+
+def test_single_image_block_causal_is_full(dit):
+    w = wl.small_workload("f", 1, 4, 4, 128, (("I", 1, 16, 20),), (16, 56, 56), seed=9)
+    d = wl.draw(w)
+    mask, shapes = wl.sequence_inputs(w)
+    m = _meta_gpu(dit, mask, shapes, "centered_fhw")
+    q, k, v = (to_device(d.bits[n], "bf16") for n in ("q", "k", "v"))
+    a = dit.forward(q, k, v, "block_causal", m)
+    b = dit.forward(q, k, v, "full")
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_empty_and_unit_inputs(dit):
+    q = torch.zeros(0, 16, 4, 128, dtype=torch.bfloat16, device="cuda")
+    o = dit.forward(q, q[:, :, :2], q[:, :, :2], "full")
+    assert o.shape == q.shape
+    q = torch.zeros(2, 0, 4, 128, dtype=torch.bfloat16, device="cuda")
+    o = dit.forward(q, q, q, "full")
+    assert o.shape == q.shape
+    # one token: the output is its own value row
+    v = torch.randn(1, 1, 2, 128, device="cuda").to(torch.bfloat16)
+    qk = torch.randn(1, 1, 2, 128, device="cuda").to(torch.bfloat16)
+    o = dit.forward(qk, qk, v, "full")
+    torch.cuda.synchronize()
+    assert torch.equal(o, v)
