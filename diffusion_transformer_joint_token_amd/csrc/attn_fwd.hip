@@ -64,7 +64,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   constexpr int CHUNKS = DP / 8;   // 16-byte chunks per key row actually used
   constexpr int LOADS = (kTileN * 16) / (NW * 64);  // LDS-load instructions per wave per tile
 
-  __shared__ __attribute__((aligned(1024))) char smem[2][2][kTileBytes];  // [buffer][K|V]
+  // Two pipeline stages in distinct LDS objects, so the compiler can tell the
+  // stage being filled from the stage being read and does not make the reads
+  // wait for the prefetch.
+  __shared__ __attribute__((aligned(1024))) char sK0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char sV0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char sK1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char sV1[kTileBytes];
   __shared__ int s_lim[NW];
 
   const int lane = threadIdx.x & 63;
@@ -77,12 +83,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   const int b = bh / a.H;
   const int kvh = h / (a.H / a.Hk);
   const int Sk = a.Sk;
+  const int P = a.P;
 
   // This lane's query row and its key bound.
   const int qrow = qtile * 32 * NW + wave * 32 + (lane & 31);
   const bool row_ok = qrow < a.Snew;
   const int qclamp = row_ok ? qrow : a.Snew - 1;
-  const int lim = a.kv_limit ? a.kv_limit[a.P + qclamp] : Sk;
+  const int lim = a.kv_limit ? a.kv_limit[P + qclamp] : Sk;
   int wlim_max = lim, wlim_min = lim;
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) {
@@ -112,34 +119,35 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
 
   // Global -> LDS loader.  Position p = 64*(i*NW + wave) + lane of a tile is
   // row p/16, physical chunk p%16, which holds logical chunk (p%16) ^ swz(row).
+  // Everything but the key index is fixed for the whole kernel.
   const __bf16* kc = reinterpret_cast<const __bf16*>(a.kc) + b * a.kcs[0] + kvh * a.kcs[2];
   const __bf16* vc = reinterpret_cast<const __bf16*>(a.vc) + b * a.vcs[0] + kvh * a.vcs[2];
   const __bf16* kn = reinterpret_cast<const __bf16*>(a.kn) + b * a.kns[0] + kvh * a.kns[2];
   const __bf16* vn = reinterpret_cast<const __bf16*>(a.vn) + b * a.vns[0] + kvh * a.vns[2];
+  const int64_t kcs1 = a.kcs[1], vcs1 = a.vcs[1], kns1 = a.kns[1], vns1 = a.vns[1];
   const int dchunks = a.D / 8;
-  auto issue_tile = [&](int t, int buf) {
+  int lrow[LOADS], lcol[LOADS];
+  bool lact[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int p = 64 * (i * NW + wave) + lane;
+    lrow[i] = p >> 4;
+    const int c = (p & 15) ^ swz(lrow[i]);
+    lact[i] = c < CHUNKS;
+    lcol[i] = 8 * (c < dchunks ? c : 0);  // padding channels: any finite data (Q is zero there)
+  }
+  auto issue_tile = [&](int t, char* kdst, char* vdst) {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      const int p = 64 * (i * NW + wave) + lane;
-      const int row = p >> 4;
-      const int c = (p & 15) ^ swz(row);
-      if (c < CHUNKS) {
-        int key = t * kTileN + row;
+      if (lact[i]) {
+        int key = t * kTileN + lrow[i];
         key = key < Sk ? key : Sk - 1;
-        const int cs = c < dchunks ? c : 0;  // padding channels: any finite data (Q is zero there)
-        const __bf16* ks;
-        const __bf16* vs;
-        if (key < a.P) {
-          ks = kc + (int64_t)key * a.kcs[1];
-          vs = vc + (int64_t)key * a.vcs[1];
-        } else {
-          ks = kn + (int64_t)(key - a.P) * a.kns[1];
-          vs = vn + (int64_t)(key - a.P) * a.vns[1];
-        }
-        lds_void* kdst = (lds_void*)(&smem[buf][0][64 * 16 * (i * NW + wave)]);
-        lds_void* vdst = (lds_void*)(&smem[buf][1][64 * 16 * (i * NW + wave)]);
-        __builtin_amdgcn_global_load_lds(ks + 8 * cs, kdst, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vs + 8 * cs, vdst, 16, 0, 0);
+        const bool cached = key < P;
+        const int kk = cached ? key : key - P;
+        const __bf16* ks = (cached ? kc + kk * kcs1 : kn + kk * kns1) + lcol[i];
+        const __bf16* vs = (cached ? vc + kk * vcs1 : vn + kk * vns1) + lcol[i];
+        __builtin_amdgcn_global_load_lds(ks, (lds_void*)(kdst + 1024 * (i * NW + wave)), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vs, (lds_void*)(vdst + 1024 * (i * NW + wave)), 16, 0, 0);
       }
     }
   };
@@ -151,15 +159,21 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   float m_cur = -INFINITY;  // running max of the raw logits (unscaled)
   float l_part = 0.f;       // this lane's share of the row sum
 
-  if (n_tiles > 0) issue_tile(0, 0);
-  for (int t = 0; t < n_tiles; ++t) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (t + 1 < n_tiles) issue_tile(t + 1, (t + 1) & 1);
+  // Per-lane LDS byte offsets that do not depend on the tile.
+  int k_off[KSTEPS][2];
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int row = 32 * kb + (lane & 31);
+      k_off[ks][kb] = row * kRowBytes + (((2 * ks + g) ^ swz(row)) << 4);
+    }
+  const int G = lane >> 4;
+  const int il = lane & 15;
+
+  auto compute_tile = [&](int t, const char* kt, const char* vt) {
     const int k0 = t * kTileN;
-    if (k0 >= wlim_max) continue;  // wave-uniform: nothing allowed in this tile
-    const char* kt = smem[t & 1][0];
-    const char* vt = smem[t & 1][1];
+    if (k0 >= wlim_max) return;  // wave-uniform: nothing allowed in this tile
 
     // S^T for two 32-key blocks.
     f32x16 sacc[2] = {f32x16{}, f32x16{}};
@@ -167,9 +181,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
     for (int ks = 0; ks < KSTEPS; ++ks) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const int row = 32 * kb + (lane & 31);
-        const int pc = (2 * ks + g) ^ swz(row);
-        const bf16x8 kop = *reinterpret_cast<const bf16x8*>(kt + row * kRowBytes + pc * 16);
+        const bf16x8 kop = *reinterpret_cast<const bf16x8*>(kt + k_off[ks][kb]);
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[ks], sacc[kb], 0, 0, 0);
       }
     }
@@ -227,8 +239,6 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
     }
 
     // O^T += V^T P^T.
-    const int G = lane >> 4;
-    const int il = lane & 15;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -251,6 +261,20 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
         }
       }
     }
+  };
+
+  // Two-stage pipeline, unrolled by two so each stage is named statically.
+  if (n_tiles > 0) issue_tile(0, sK0, sV0);
+  for (int t = 0; t < n_tiles; t += 2) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (t + 1 < n_tiles) issue_tile(t + 1, sK1, sV1);
+    compute_tile(t, sK0, sV0);
+    if (t + 1 >= n_tiles) break;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (t + 2 < n_tiles) issue_tile(t + 2, sK0, sV0);
+    compute_tile(t + 1, sK1, sV1);
   }
 
   // Normalise and store: lane holds query (lane & 31), channels
