@@ -193,6 +193,9 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=list(wl.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the host oracle timing")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB five times (the reference "
+                         "kernel that scales the FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -203,6 +206,16 @@ def main(argv=None) -> int:
     if not torch.cuda.is_available():
         print("bench.py needs an MI355X GPU (none visible)", file=sys.stderr)
         return 2
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copied %d bytes five times" % n)
+        return 0
 
     w = wl.WORKLOADS[args.workload]
     log("workload %s: B=%d H=%d/%d D=%d S=%d (queries %d) mask=%s dtype=%s" % (

@@ -178,6 +178,10 @@ static int attention_common(const void* q, const void* kc, const void* vc, const
     return DIT_ATTN_ERR_ALIGN;
   if (P > 0 && (!rows_aligned(kc, st[1], es) || !rows_aligned(vc, st[2], es))) return DIT_ATTN_ERR_ALIGN;
   if (B == 0 || S_new == 0) return DIT_ATTN_OK;
+  // Keys are addressed with 32-bit byte offsets inside one (batch, kv-head) slice.
+  const int64_t span_new = (int64_t)S_new * std::max(st[3][1], st[4][1]) * es;
+  const int64_t span_cache = (int64_t)P * std::max(st[1][1], st[2][1]) * es;
+  if (span_new >= INT32_MAX || span_cache >= INT32_MAX) return DIT_ATTN_ERR_UNSUPPORTED;
   const int64_t blocks = ((int64_t)S_new + 127) / 128 * B * H;
   if (blocks > INT32_MAX || ((int64_t)S_new + 63) / 64 * B * H > INT32_MAX) return DIT_ATTN_ERR_UNSUPPORTED;
 

@@ -56,6 +56,15 @@ __device__ __forceinline__ void map_block(int id, int nblocks, int n_qtiles, int
   qtile = n_qtiles - 1 - (logical - bh * n_qtiles);
 }
 
+// Buffer resource word 3 for untyped 32-bit accesses on gfx9-class parts.
+constexpr int kRsrcWord3 = 0x00020000;
+
+// 16 bytes per lane from a buffer resource straight into LDS (lane i lands at
+// dst + 16 i); an offset past the resource's extent reads as zeros.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, char* dst, int voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 16, voffset, 0, 0, 0);
+}
+
 template <int DP, int NW>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   static_assert(DP % 32 == 0 && DP <= 128, "padded head dim");
@@ -64,12 +73,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   constexpr int CHUNKS = DP / 8;   // 16-byte chunks per key row actually used
   constexpr int LOADS = (kTileN * 16) / (NW * 64);  // LDS-load instructions per wave per tile
 
-  // Two pipeline stages in distinct LDS objects, so the compiler can tell the
-  // stage being filled from the stage being read and does not make the reads
-  // wait for the prefetch.
+  // Two K stages and two V stages, each a distinct LDS object, so the compiler
+  // can tell the stage being filled from the stage being read.  K runs one
+  // tile ahead of V: iteration t reads K(t+1) (for S(t+1)) and V(t) (for PV(t)).
   __shared__ __attribute__((aligned(1024))) char sK0[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char sV0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char sK1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char sV0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char sV1[kTileBytes];
   __shared__ int s_lim[NW];
 
@@ -111,20 +120,23 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
         qreg[ks] = bf16x8{};
     }
   }
-  __syncthreads();
-  int wg_lim = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) wg_lim = max(wg_lim, s_lim[w]);
-  const int n_tiles = (wg_lim + kTileN - 1) / kTileN;
 
-  // Global -> LDS loader.  Position p = 64*(i*NW + wave) + lane of a tile is
-  // row p/16, physical chunk p%16, which holds logical chunk (p%16) ^ swz(row).
-  // Everything but the key index is fixed for the whole kernel.
+  // Global -> LDS loader on buffer resources (one per K/V source), so a
+  // tile costs one address add per load.  Position p = 64*(i*NW + wave) + lane
+  // of a tile is row p/16, physical chunk p%16, holding logical chunk
+  // (p%16) ^ swz(row).  Rows past the end of a source read as zeros.
+  const int ke = 2;  // bytes per element
   const __bf16* kc = reinterpret_cast<const __bf16*>(a.kc) + b * a.kcs[0] + kvh * a.kcs[2];
   const __bf16* vc = reinterpret_cast<const __bf16*>(a.vc) + b * a.vcs[0] + kvh * a.vcs[2];
   const __bf16* kn = reinterpret_cast<const __bf16*>(a.kn) + b * a.kns[0] + kvh * a.kns[2];
   const __bf16* vn = reinterpret_cast<const __bf16*>(a.vn) + b * a.vns[0] + kvh * a.vns[2];
-  const int64_t kcs1 = a.kcs[1], vcs1 = a.vcs[1], kns1 = a.kns[1], vns1 = a.vns[1];
+  const int rkc = (int)a.kcs[1] * ke, rvc = (int)a.vcs[1] * ke;  // row strides in bytes
+  const int rkn = (int)a.kns[1] * ke, rvn = (int)a.vns[1] * ke;
+  const int rowbytes = a.D * ke;
+  const __amdgpu_buffer_rsrc_t rs_kc = __builtin_amdgcn_make_buffer_rsrc((void*)kc, 0, P > 0 ? (P - 1) * rkc + rowbytes : 0, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rs_vc = __builtin_amdgcn_make_buffer_rsrc((void*)vc, 0, P > 0 ? (P - 1) * rvc + rowbytes : 0, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rs_kn = __builtin_amdgcn_make_buffer_rsrc((void*)kn, 0, (a.Snew - 1) * rkn + rowbytes, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rs_vn = __builtin_amdgcn_make_buffer_rsrc((void*)vn, 0, (a.Snew - 1) * rvn + rowbytes, kRsrcWord3);
   const int dchunks = a.D / 8;
   int lrow[LOADS], lcol[LOADS];
   bool lact[LOADS];
@@ -134,23 +146,59 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
     lrow[i] = p >> 4;
     const int c = (p & 15) ^ swz(lrow[i]);
     lact[i] = c < CHUNKS;
-    lcol[i] = 8 * (c < dchunks ? c : 0);  // padding channels: any finite data (Q is zero there)
+    lcol[i] = 16 * (c < dchunks ? c : 0);  // padding channels: any finite data (Q is zero there)
   }
-  auto issue_tile = [&](int t, char* kdst, char* vdst) {
+  // One source: keys [k0, k0 + 64) all cached (k0 + 64 <= P) or all new (k0 >= P).
+  // Otherwise (the tile holding key P) each lane picks its own source.
+  auto issue = [&](int t, char* dst, bool is_k) {
+    const int k0 = t * kTileN;
+    const __amdgpu_buffer_rsrc_t rc = is_k ? rs_kc : rs_vc;
+    const __amdgpu_buffer_rsrc_t rn = is_k ? rs_kn : rs_vn;
+    const int sc = is_k ? rkc : rvc;
+    const int sn = is_k ? rkn : rvn;
+    if (k0 + kTileN <= P) {
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      if (lact[i]) {
-        int key = t * kTileN + lrow[i];
-        key = key < Sk ? key : Sk - 1;
-        const bool cached = key < P;
-        const int kk = cached ? key : key - P;
-        const __bf16* ks = (cached ? kc + kk * kcs1 : kn + kk * kns1) + lcol[i];
-        const __bf16* vs = (cached ? vc + kk * vcs1 : vn + kk * vns1) + lcol[i];
-        __builtin_amdgcn_global_load_lds(ks, (lds_void*)(kdst + 1024 * (i * NW + wave)), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vs, (lds_void*)(vdst + 1024 * (i * NW + wave)), 16, 0, 0);
+      for (int i = 0; i < LOADS; ++i)
+        if (lact[i])
+          dma16(rc, dst + 1024 * (i * NW + wave), (k0 + lrow[i]) * sc + lcol[i]);
+    } else if (k0 >= P) {
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i)
+        if (lact[i])
+          dma16(rn, dst + 1024 * (i * NW + wave), (k0 - P + lrow[i]) * sn + lcol[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const int key = k0 + lrow[i];
+        if (lact[i] && key < P)
+          dma16(rc, dst + 1024 * (i * NW + wave), key * sc + lcol[i]);
+        if (lact[i] && key >= P)
+          dma16(rn, dst + 1024 * (i * NW + wave), (key - P) * sn + lcol[i]);
       }
     }
   };
+
+  // Per-lane LDS byte offsets that do not depend on the tile.
+  int k_off[KSTEPS];
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) {
+    const int row = lane & 31;  // +32 rows (8192 bytes) for the second key block
+    k_off[ks] = row * kRowBytes + (((2 * ks + g) ^ swz(row)) << 4);
+  }
+  const int G = lane >> 4;
+  const int il = lane & 15;
+  int v_off[MBLK][2];
+#pragma unroll
+  for (int mb = 0; mb < MBLK; ++mb) {
+    const int d = 32 * mb + 16 * (G & 1) + 4 * (il & 3);
+    const int c = d >> 3;
+    const int hb = ((d >> 2) & 1) * 8;
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      const int key = 4 * (G >> 1) + (il >> 2) + 8 * hi;  // +16 (half) and +32 (kb) keep swz
+      v_off[mb][hi] = key * kRowBytes + ((c ^ swz(key)) << 4) + hb;
+    }
+  }
 
   f32x16 oacc[MBLK];
 #pragma unroll
@@ -159,68 +207,40 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   float m_cur = -INFINITY;  // running max of the raw logits (unscaled)
   float l_part = 0.f;       // this lane's share of the row sum
 
-  // Per-lane LDS byte offsets that do not depend on the tile.
-  int k_off[KSTEPS][2];
-#pragma unroll
-  for (int ks = 0; ks < KSTEPS; ++ks)
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int row = 32 * kb + (lane & 31);
-      k_off[ks][kb] = row * kRowBytes + (((2 * ks + g) ^ swz(row)) << 4);
-    }
-  const int G = lane >> 4;
-  const int il = lane & 15;
-
-  auto compute_tile = [&](int t, const char* kt, const char* vt) {
-    const int k0 = t * kTileN;
-    if (k0 >= wlim_max) return;  // wave-uniform: nothing allowed in this tile
-
-    // S^T for two 32-key blocks.
-    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+  // S^T = K Q^T for the 64 keys of a K stage (two 32-key blocks).
+  auto qk = [&](const char* kt, f32x16 (&sacc)[2]) {
+    sacc[0] = f32x16{};
+    sacc[1] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 kop = *reinterpret_cast<const bf16x8*>(kt + k_off[ks][kb]);
+        const bf16x8 kop = *reinterpret_cast<const bf16x8*>(kt + k_off[ks] + kb * 32 * kRowBytes);
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[ks], sacc[kb], 0, 0, 0);
       }
     }
-
-    // Mask near the diagonal (or past the end of the keys).
-    if (k0 + kTileN > wlim_min) {
+  };
+  // Mask keys >= this row's bound (only tiles that reach past a wave's smallest bound).
+  auto mask = [&](int t, f32x16 (&sacc)[2]) {
+    const int k0 = t * kTileN;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = k0 + 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
-          if (key >= lim) sacc[kb][i] = -INFINITY;
-        }
+      for (int i = 0; i < 16; ++i) {
+        const int key = k0 + 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
+        if (key >= lim) sacc[kb][i] = -INFINITY;
       }
-    }
-
-    // Row max (this lane's 32 keys, then the partner lane's 32).
+  };
+  auto rowmax = [&](const f32x16 (&sacc)[2]) {
     float mx = sacc[0][0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[0][i]);
 #pragma unroll
     for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[1][i]);
-    mx = max_with_partner32(mx);
-    const bool grow = (mx - m_cur) * c2 > kLazyRescale;
-    if (__any(grow)) {
-      // Only the rows that grew move their max (alpha = 1 elsewhere), so a
-      // row's result never depends on the other rows of its wave.
-      const float m_new = grow ? mx : m_cur;
-      const float alpha = __builtin_amdgcn_exp2f((m_cur - m_new) * c2);
-      l_part *= alpha;
-#pragma unroll
-      for (int mb = 0; mb < MBLK; ++mb) oacc[mb] *= alpha;
-      m_cur = m_new;
-    }
-    // A row with no allowed key so far keeps m = -inf; its p must be 0, not NaN.
-    const float mc = (m_cur == -INFINITY) ? 0.f : m_cur * c2;
-
-    // P = exp2(s * c2 - m * c2), row sums, bf16 B operands for PV.
-    bf16x8 pop[2][2];
+    return max_with_partner32(mx);
+  };
+  // P = exp2(s * c2 - m * c2) as bf16 B operands; this lane's row-sum share.
+  auto softmax = [&](const f32x16 (&sacc)[2], float mc, bf16x8 (&pop)[2][2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -237,23 +257,20 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
         pop[kb][half] = __builtin_bit_cast(bf16x8, w);
       }
     }
-
-    // O^T += V^T P^T.
+  };
+  // O^T += V^T P^T for the 64 keys of a V stage.
+  auto pv = [&](const char* vt, const bf16x8 (&pop)[2][2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        const int key_lo = 32 * kb + 16 * half + 4 * (G >> 1) + (il >> 2);
-        const int key_hi = key_lo + 8;
+        const int shift = (32 * kb + 16 * half) * kRowBytes;
 #pragma unroll
         for (int mb = 0; mb < MBLK; ++mb) {
-          const int d = 32 * mb + 16 * (G & 1) + 4 * (il & 3);
-          const int c = d >> 3;
-          const int hb = ((d >> 2) & 1) * 8;
-          const lds_void* p_lo = (const lds_void*)(vt + key_lo * kRowBytes + ((c ^ swz(key_lo)) << 4) + hb);
-          const lds_void* p_hi = (const lds_void*)(vt + key_hi * kRowBytes + ((c ^ swz(key_hi)) << 4) + hb);
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p_lo);
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p_hi);
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(lds_void*)(vt + v_off[mb][0] + shift));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(lds_void*)(vt + v_off[mb][1] + shift));
           const u32x4 vw = {__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
                             __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
           oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vw), pop[kb][half],
@@ -262,19 +279,95 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
       }
     }
   };
+  // Move the running max where a row's tile max exceeds it by more than the
+  // lazy threshold; only those rows rescale (alpha = 1 elsewhere), so a row's
+  // result never depends on the other rows of its wave.
+  auto update_max = [&](float mx) {
+    const bool grow = (mx - m_cur) * c2 > kLazyRescale;
+    if (__any(grow)) {
+      const float m_new = grow ? mx : m_cur;
+      const float alpha = __builtin_amdgcn_exp2f((m_cur - m_new) * c2);
+      l_part *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < MBLK; ++mb) oacc[mb] *= alpha;
+      m_cur = m_new;
+    }
+    // A row with no allowed key so far keeps m = -inf; its p must be 0, not NaN.
+    return (m_cur == -INFINITY) ? 0.f : m_cur * c2;
+  };
 
-  // Two-stage pipeline, unrolled by two so each stage is named statically.
-  if (n_tiles > 0) issue_tile(0, sK0, sV0);
+  // One iteration: S(t) (masked, its row max mx) is in registers, K(t+1) and
+  // V(t) are in LDS.  Softmax of tile t runs interleaved with the QK^T MFMAs of
+  // tile t+1, then PV of tile t interleaved with the row max of tile t+1.
+  f32x16 s_cur[2], s_nxt[2];
+  float mx_cur = -INFINITY;
+  auto step = [&](int t, const char* k_next, const char* v_cur) {
+    const int k0 = t * kTileN;
+    if (k0 >= wlim_max) return;  // wave-uniform: nothing allowed from here on
+    const float mc = update_max(mx_cur);
+    bf16x8 pop[2][2];
+    const int k1 = k0 + kTileN;
+    const bool has_next = (t + 1) * kTileN < wlim_max && k1 < Sk;
+    if (has_next) {
+      softmax(s_cur, mc, pop);
+      qk(k_next, s_nxt);
+#pragma unroll
+      for (int i = 0; i < 2 * KSTEPS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read (K operand)
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+      }
+      if (k1 + kTileN > wlim_min) {
+        pv(v_cur, pop);
+        mask(t + 1, s_nxt);
+        mx_cur = rowmax(s_nxt);
+      } else {
+        pv(v_cur, pop);
+        mx_cur = rowmax(s_nxt);
+#pragma unroll
+        for (int i = 0; i < 4 * MBLK; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read (V^T, transposed)
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+        }
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
+    } else {
+      softmax(s_cur, mc, pop);
+      pv(v_cur, pop);
+    }
+  };
+
+  __syncthreads();  // s_lim
+  int wg_lim = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) wg_lim = max(wg_lim, s_lim[w]);
+  const int n_tiles = (wg_lim + kTileN - 1) / kTileN;
+
+  // Prologue: K(0), V(0), K(1) in flight; S(0) once they land.
+  issue(0, sK0, true);
+  issue(0, sV0, false);
+  if (n_tiles > 1) issue(1, sK1, true);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  qk(sK0, s_cur);
+  if (kTileN > wlim_min) mask(0, s_cur);
+  mx_cur = rowmax(s_cur);
+
+  // Stages are named statically, two iterations per trip.
   for (int t = 0; t < n_tiles; t += 2) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (t + 1 < n_tiles) issue_tile(t + 1, sK1, sV1);
-    compute_tile(t, sK0, sV0);
+    if (t + 2 < n_tiles) issue(t + 2, sK0, true);
+    if (t + 1 < n_tiles) issue(t + 1, sV1, false);
+    step(t, sK1, sV0);
     if (t + 1 >= n_tiles) break;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (t + 2 < n_tiles) issue_tile(t + 2, sK0, sV0);
-    compute_tile(t + 1, sK1, sV1);
+    if (t + 3 < n_tiles) issue(t + 3, sK1, true);
+    if (t + 2 < n_tiles) issue(t + 2, sV0, false);
+    step(t + 1, sK0, sV1);
   }
 
   // Normalise and store: lane holds query (lane & 31), channels
