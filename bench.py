@@ -185,6 +185,62 @@ def cpu_baseline(w: wl.Workload, drawn: wl.Drawn, budget_s: float = 12.0):
             "seconds": elapsed}
 
 
+def _counter_rows(path: str):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)):
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    if not rows:
+        raise SystemExit("no rocprofv3 counter_collection.csv under %s" % path)
+    return rows
+
+
+def _per_dispatch(rows, kernel_substr: str, counter: str) -> float:
+    """Mean over dispatches of one kernel of a counter summed over its instances."""
+    per = {}
+    for r in rows:
+        if kernel_substr in r["Kernel_Name"] and r["Counter_Name"] == counter:
+            per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise SystemExit("counter %s not found for kernel %s" % (counter, kernel_substr))
+    return sum(per.values()) / len(per)
+
+
+def summarize_counters(root: str, copy_mib: int, workload: str) -> int:
+    """Turn rocprofv3 --pmc runs into the HBM-traffic record bench.py reports.
+
+    Expects sub-directories of ``root``: fetch/ and write/ (FETCH_SIZE and
+    WRITE_SIZE over a bench.py run), copy_fetch/ and copy_write/ (the same
+    counters over ``bench.py --copy-calibration copy_mib``) and optionally
+    sq/ (SQ_* counters).  Each counter is scaled by (known copy bytes) /
+    (counter reading for the copy kernel)."""
+    copy_bytes = copy_mib << 20
+    cf = _per_dispatch(_counter_rows(os.path.join(root, "copy_fetch")), "copyBuffer", "FETCH_SIZE")
+    cw = _per_dispatch(_counter_rows(os.path.join(root, "copy_write")), "copyBuffer", "WRITE_SIZE")
+    fetch_scale, write_scale = copy_bytes / (cf * 1024.0), copy_bytes / (cw * 1024.0)
+    fr, wr = _counter_rows(os.path.join(root, "fetch")), _counter_rows(os.path.join(root, "write"))
+    rec = {"workload": workload, "kernel": "attn_fwd_bf16_kernel", "kernel_source_sha256": source_sha(ATTN_SOURCE),
+           "copy_bytes": copy_bytes, "copy_fetch_kib": cf, "copy_write_kib": cw, "fetch_scale": fetch_scale,
+           "write_scale": write_scale, "kernels": {}}
+    for name, key in (("attention", "attn_fwd_bf16"), ("qknorm_rope", "qknorm_rope"), ("token_metadata", "token_meta")):
+        f = _per_dispatch(fr, key, "FETCH_SIZE") * 1024.0 * fetch_scale
+        wb = _per_dispatch(wr, key, "WRITE_SIZE") * 1024.0 * write_scale
+        rec["kernels"][name] = {"fetch_bytes": f, "write_bytes": wb, "hbm_bytes": f + wb}
+    rec["hbm_bytes_per_launch"] = rec["kernels"]["attention"]["hbm_bytes"]
+    sq_dir = os.path.join(root, "sq")
+    if os.path.isdir(sq_dir):
+        sq = _counter_rows(sq_dir)
+        names = sorted({r["Counter_Name"] for r in sq})
+        rec["attention_sq"] = {n: _per_dispatch(sq, "attn_fwd_bf16", n) for n in names}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(rec, fh, indent=1, sort_keys=True)
+    print(json.dumps(rec, indent=1, sort_keys=True))
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -196,8 +252,12 @@ def main(argv=None) -> int:
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (the reference "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters) and exit")
+    ap.add_argument("--summarize-counters", metavar="DIR", default=None,
+                    help="CPU only: read rocprofv3 --pmc outputs under DIR and write the HBM-traffic record")
     args = ap.parse_args(argv)
 
+    if args.summarize_counters:
+        return summarize_counters(args.summarize_counters, args.copy_calibration or 256, args.workload)
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
