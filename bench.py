@@ -101,16 +101,19 @@ class Step:
         self.dit.build_token_metadata(self.mask, self.shapes, self.w.pos_mode, out=self.meta)
 
     def norm_rope(self):
+        # The softmax scale and log2(e) are folded into Q' here (one rounding),
+        # so the attention exponentiates its MFMA output directly.
         P = self.w.prefix_len
         self.dit.qknorm_rope(self.q, self.k, self.meta.pos_ids[P:], self.w.axes, self.w.eps, self.wq, self.wk,
-                             q_out=self.qp, k_out=self.kp)
+                             q_out=self.qp, k_out=self.kp, q_scale=self.dit.prescaled_q_factor(self.w.head_dim))
 
     def attention(self):
         if self.w.prefix_len:
             self.dit.forward_cached(self.qp, self.kc, self.vc, self.kp, self.v, self.w.mask_mode, self.meta,
-                                    out=self.o)
+                                    softmax_scale=self.dit.LN2, out=self.o)
         else:
-            self.dit.forward(self.qp, self.kp, self.v, self.w.mask_mode, self.meta, out=self.o)
+            self.dit.forward(self.qp, self.kp, self.v, self.w.mask_mode, self.meta, softmax_scale=self.dit.LN2,
+                             out=self.o)
 
     def run(self):
         self.metadata()

@@ -40,7 +40,7 @@ def _load() -> ctypes.CDLL:
                                                   ctypes.POINTER(TokenMetaStruct), vp, vp]
     lib.dit_attn_qknorm_rope.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                          Strides3, Strides3, Strides3, Strides3, vp, i32,
-                                         ctypes.POINTER(i32), f32, f32, i32, vp]
+                                         ctypes.POINTER(i32), f32, f32, f32, i32, vp]
     lib.dit_attn_forward.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, Strides3 * 4, i32,
                                      ctypes.POINTER(TokenMetaStruct), f32, i32, vp]
     lib.dit_attn_forward_cached.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,

@@ -16,11 +16,22 @@ import torch
 from . import _lib
 from ._lib import DitAttnError, check, lib
 
-__all__ = ["TokenMeta", "DitAttnError", "dit_attn_build_token_metadata", "dit_attn_qknorm_rope",
+__all__ = ["TokenMeta", "DitAttnError", "LN2", "LOG2E", "prescaled_q_factor", "dit_attn_build_token_metadata", "dit_attn_qknorm_rope",
            "dit_attn_forward", "dit_attn_forward_cached", "build_token_metadata", "qknorm_rope", "forward",
            "forward_cached"]
 
 _POS = {"centered_fhw": _lib.POS_CENTERED_FHW, "grid_hw": _lib.POS_GRID_HW}
+
+LOG2E = 1.4426950408889634
+LN2 = 0.6931471805599453
+
+
+def prescaled_q_factor(head_dim: int, softmax_scale: Optional[float] = None) -> float:
+    """q_scale for dit_attn_qknorm_rope that folds the softmax scale (default
+    1/sqrt(head_dim)) and log2(e) into Q; then call the attention with
+    softmax_scale=LN2."""
+    scale = softmax_scale if softmax_scale else 1.0 / math.sqrt(head_dim)
+    return scale * LOG2E
 _MASK = {"full": _lib.MASK_FULL, "block_causal": _lib.MASK_BLOCK_CAUSAL}
 
 
@@ -105,7 +116,8 @@ def dit_attn_qknorm_rope(q: torch.Tensor, k: torch.Tensor, pos_ids: torch.Tensor
                          eps: float, q_weight: Optional[torch.Tensor] = None,
                          k_weight: Optional[torch.Tensor] = None, rope_theta: float = 10000.0,
                          q_out: Optional[torch.Tensor] = None, k_out: Optional[torch.Tensor] = None,
-                         inplace: bool = False, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+                         inplace: bool = False, q_scale: float = 1.0,
+                         stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
     if inplace:
         q_out, k_out = q, k
     if q_out is None:
@@ -128,7 +140,8 @@ def dit_attn_qknorm_rope(q: torch.Tensor, k: torch.Tensor, pos_ids: torch.Tensor
     st = lib.dit_attn_qknorm_rope(q.data_ptr(), k.data_ptr(), q_out.data_ptr(), k_out.data_ptr(), _ptr(q_weight),
                                   _ptr(k_weight), B, S, H, Hk, D, _bshd_strides(q, "q"), _bshd_strides(k, "k"),
                                   _bshd_strides(q_out, "q_out"), _bshd_strides(k_out, "k_out"), pos_ids.data_ptr(),
-                                  len(axes_dims), axes, float(rope_theta), float(eps), dt, _stream(stream))
+                                  len(axes_dims), axes, float(rope_theta), float(eps), float(q_scale), dt,
+                                  _stream(stream))
     check(st, "dit_attn_qknorm_rope")
     return q_out, k_out
 

@@ -92,7 +92,8 @@ int dit_attn_qknorm_rope(const void* q, const void* k, void* q_out, void* k_out,
                          const void* k_weight, int32_t B, int32_t S, int32_t H, int32_t H_kv, int32_t D,
                          const int64_t q_strides[3], const int64_t k_strides[3], const int64_t qo_strides[3],
                          const int64_t ko_strides[3], const int32_t* pos_ids, int32_t n_axes,
-                         const int32_t* axes_dims, float rope_theta, float eps, int32_t dtype, void* stream) {
+                         const int32_t* axes_dims, float rope_theta, float eps, float q_scale, int32_t dtype,
+                         void* stream) {
   if (B < 0 || S < 0) return DIT_ATTN_ERR_SHAPE;
   if (B == 0 || S == 0) return DIT_ATTN_OK;  // nothing to do; no pointer is read
   if (!q || !k || !q_out || !k_out || !pos_ids || !axes_dims || !q_strides || !k_strides || !qo_strides ||
@@ -110,7 +111,8 @@ int dit_attn_qknorm_rope(const void* q, const void* k, void* q_out, void* k_out,
     sum += axes_dims[i];
   }
   if (sum != D) return DIT_ATTN_ERR_SHAPE;
-  if (!(rope_theta > 0.f) || !std::isfinite(rope_theta) || !(eps >= 0.f) || !std::isfinite(eps))
+  if (!(rope_theta > 0.f) || !std::isfinite(rope_theta) || !(eps >= 0.f) || !std::isfinite(eps) ||
+      !std::isfinite(q_scale) || q_scale == 0.f)
     return DIT_ATTN_ERR_SHAPE;
   if (!strides_ok(q_strides) || !strides_ok(k_strides) || !strides_ok(qo_strides) || !strides_ok(ko_strides))
     return DIT_ATTN_ERR_SHAPE;
@@ -140,6 +142,7 @@ int dit_attn_qknorm_rope(const void* q, const void* k, void* q_out, void* k_out,
   a.Hk = H_kv;
   a.D = D;
   a.eps = eps;
+  a.q_scale = q_scale;
   int p = 0;
   for (int ax = 0; ax < n_axes; ++ax) {
     const int da = axes_dims[ax];

@@ -31,6 +31,8 @@
 //  * Work-groups are ordered heaviest query tile first and mapped so that all
 //    query tiles of one (batch, head) share an XCD (and its L2).
 
+#include <cmath>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -42,6 +44,8 @@ constexpr int kTileN = 64;        // keys per tile
 constexpr int kRowBytes = 256;    // LDS bytes per key row (16 chunks of 16 B)
 constexpr int kTileBytes = kTileN * kRowBytes;
 constexpr float kLazyRescale = 8.0f;  // log2 units
+constexpr int PF_K = 3;  // K operands read this many MFMAs ahead
+constexpr int PF_V = 2;  // V^T operands read this many MFMAs ahead
 
 __device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 
@@ -59,13 +63,21 @@ __device__ __forceinline__ void map_block(int id, int nblocks, int n_qtiles, int
 // Buffer resource word 3 for untyped 32-bit accesses on gfx9-class parts.
 constexpr int kRsrcWord3 = 0x00020000;
 
+// acc + lo + hi of a packed bf16 pair, in one v_dot2 against (1, 1).
+__device__ __forceinline__ float add_bf16_pair(uint32_t pair, float acc) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), one, acc, false);
+}
+
 // 16 bytes per lane from a buffer resource straight into LDS (lane i lands at
 // dst + 16 i); an offset past the resource's extent reads as zeros.
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, char* dst, int voffset) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 16, voffset, 0, 0, 0);
 }
 
-template <int DP, int NW>
+// UNIT: Q already carries softmax_scale * log2(e) (scale argument ln 2), so the
+// MFMA output is the exponent itself.
+template <int DP, int NW, bool UNIT>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   static_assert(DP % 32 == 0 && DP <= 128, "padded head dim");
   constexpr int KSTEPS = DP / 16;  // QK^T contraction steps
@@ -200,17 +212,28 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
     }
   }
 
+  // Softmax bookkeeping.  m_off (log2 units) is this row's offset; every S
+  // tile's accumulator starts at -m_off (in logit units), so the MFMA yields
+  // logits minus the offset in effect when the tile was computed.  The offset
+  // only moves when a tile's max exceeds it by more than the lazy threshold,
+  // so probabilities stay <= 2^8 and O is rarely rescaled; only the rows that
+  // grew move, so a row's result never depends on the other rows of its wave.
   f32x16 oacc[MBLK];
 #pragma unroll
   for (int mb = 0; mb < MBLK; ++mb) oacc[mb] = f32x16{};
-  const float c2 = a.scale * 1.4426950408889634f;  // scale * log2(e)
-  float m_cur = -INFINITY;  // running max of the raw logits (unscaled)
-  float l_part = 0.f;       // this lane's share of the row sum
+  const float c2 = a.scale * 1.4426950408889634f;  // scale * log2(e); 1 when UNIT
+  const float ic2 = UNIT ? 1.0f : 1.0f / c2;
+  float m_off = 0.f;   // running offset (log2 units)
+  bool fresh = true;   // no tile seen yet: the first one sets the offset
+  float l_part = 0.f;  // this lane's share of the row sum
 
-  // S^T = K Q^T for the 64 keys of a K stage (two 32-key blocks).
+  // S^T (logits minus the offset, logit units) for the 64 keys of a K stage.
   auto qk = [&](const char* kt, f32x16 (&sacc)[2]) {
-    sacc[0] = f32x16{};
-    sacc[1] = f32x16{};
+    const float init = -m_off * ic2;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[kb][i] = init;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
 #pragma unroll
@@ -239,25 +262,43 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
     for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[1][i]);
     return max_with_partner32(mx);
   };
-  // P = exp2(s * c2 - m * c2) as bf16 B operands; this lane's row-sum share.
-  auto softmax = [&](const f32x16 (&sacc)[2], float mc, bf16x8 (&pop)[2][2]) {
+  // mx: max of the tile's shifted logits (logit units).  Rows that grew past
+  // the threshold (or see their first tile) move the offset to the tile max,
+  // rescale O and l, and shift the tile's logits to the new offset.
+  auto update = [&](float mx, f32x16 (&sacc)[2]) {
+    const bool grow = mx > -INFINITY && (fresh || mx * c2 > kLazyRescale);
+    if (__any(grow)) {
+      const float d = grow ? mx : 0.f;
+      const float alpha = fresh ? 0.f : __builtin_amdgcn_exp2f(-d * c2);
+      l_part *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < MBLK; ++mb) oacc[mb] *= alpha;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) sacc[kb] -= d;
+      m_off += d * c2;
+    }
+    fresh = false;
+  };
+  // P = exp2(c2 * S) as bf16 B operands; row sums from the same bf16 values.
+  auto softmax = [&](const f32x16 (&sacc)[2], bf16x8 (&pop)[2][2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        float pv[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          pv[j] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][8 * half + j], c2, -mc));
-          l_part += pv[j];
-        }
         u32x4 w;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) w[j] = pack_bf16x2(pv[2 * j], pv[2 * j + 1]);
+        for (int j = 0; j < 4; ++j) {
+          const float x0 = sacc[kb][8 * half + 2 * j], x1 = sacc[kb][8 * half + 2 * j + 1];
+          w[j] = pack_bf16x2(__builtin_amdgcn_exp2f(UNIT ? x0 : x0 * c2), __builtin_amdgcn_exp2f(UNIT ? x1 : x1 * c2));
+          l_part = add_bf16_pair(w[j], l_part);
+        }
         pop[kb][half] = __builtin_bit_cast(bf16x8, w);
       }
     }
   };
+  // One iteration: S(t) (masked, its row max mx) is in registers, K(t+1) and
+  // V(t) are in LDS.  Softmax of tile t runs interleaved with the QK^T MFMAs of
+  // tile t+1, then PV of tile t interleaved with the row max of tile t+1.
   // O^T += V^T P^T for the 64 keys of a V stage.
   auto pv = [&](const char* vt, const bf16x8 (&pop)[2][2]) {
 #pragma unroll
@@ -279,43 +320,33 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
       }
     }
   };
-  // Move the running max where a row's tile max exceeds it by more than the
-  // lazy threshold; only those rows rescale (alpha = 1 elsewhere), so a row's
-  // result never depends on the other rows of its wave.
-  auto update_max = [&](float mx) {
-    const bool grow = (mx - m_cur) * c2 > kLazyRescale;
-    if (__any(grow)) {
-      const float m_new = grow ? mx : m_cur;
-      const float alpha = __builtin_amdgcn_exp2f((m_cur - m_new) * c2);
-      l_part *= alpha;
-#pragma unroll
-      for (int mb = 0; mb < MBLK; ++mb) oacc[mb] *= alpha;
-      m_cur = m_new;
-    }
-    // A row with no allowed key so far keeps m = -inf; its p must be 0, not NaN.
-    return (m_cur == -INFINITY) ? 0.f : m_cur * c2;
-  };
 
-  // One iteration: S(t) (masked, its row max mx) is in registers, K(t+1) and
-  // V(t) are in LDS.  Softmax of tile t runs interleaved with the QK^T MFMAs of
-  // tile t+1, then PV of tile t interleaved with the row max of tile t+1.
+  // One iteration: S(t) (masked, shifted, its max mx_cur) is in s_cur, K(t+1)
+  // and V(t) are in LDS.  Softmax of tile t runs interleaved with the QK^T
+  // MFMAs of tile t+1, then PV of tile t with the row max of tile t+1.
   f32x16 s_cur[2], s_nxt[2];
   float mx_cur = -INFINITY;
   auto step = [&](int t, const char* k_next, const char* v_cur) {
     const int k0 = t * kTileN;
     if (k0 >= wlim_max) return;  // wave-uniform: nothing allowed from here on
-    const float mc = update_max(mx_cur);
+    update(mx_cur, s_cur);
     bf16x8 pop[2][2];
     const int k1 = k0 + kTileN;
     const bool has_next = (t + 1) * kTileN < wlim_max && k1 < Sk;
     if (has_next) {
-      softmax(s_cur, mc, pop);
+      softmax(s_cur, pop);
       qk(k_next, s_nxt);
+      __builtin_amdgcn_sched_group_barrier(0x100, PF_K, 0);  // DS read (K operand) ahead
 #pragma unroll
-      for (int i = 0; i < 2 * KSTEPS; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read (K operand)
+      for (int i = 0; i < 2 * KSTEPS - PF_K; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+      }
+#pragma unroll
+      for (int i = 0; i < PF_K; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
       }
       if (k1 + kTileN > wlim_min) {
         pv(v_cur, pop);
@@ -324,17 +355,23 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
       } else {
         pv(v_cur, pop);
         mx_cur = rowmax(s_nxt);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF_V, 0);  // V^T reads ahead
 #pragma unroll
-        for (int i = 0; i < 4 * MBLK; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read (V^T, transposed)
+        for (int i = 0; i < 4 * MBLK - PF_V; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read (transposed)
           __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+        }
+#pragma unroll
+        for (int i = 0; i < PF_V; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
         }
       }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
     } else {
-      softmax(s_cur, mc, pop);
+      softmax(s_cur, pop);
       pv(v_cur, pop);
     }
   };
@@ -390,7 +427,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
       }
     }
     if (a.lse != nullptr && g == 0)
-      a.lse[((int64_t)b * a.H + h) * a.Snew + qrow] = m_cur * a.scale + logf(l_tot);
+      a.lse[((int64_t)b * a.H + h) * a.Snew + qrow] = (m_off + __log2f(l_tot)) * 0.6931471805599453f;
   }
 }
 
@@ -483,7 +520,12 @@ hipError_t launch_bf16(const AttnArgs& a, hipStream_t stream) {
   constexpr int NW = 4;
   const int n_qtiles = (a.Snew + 32 * NW - 1) / (32 * NW);
   const long long nblocks = (long long)n_qtiles * a.B * a.H;
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<DP, NW>), dim3((unsigned)nblocks), dim3(NW * 64), 0, stream, a);
+  // Q pre-scaled by scale * log2(e): the scale argument is ln 2 (to rounding).
+  const bool unit = std::fabs((double)a.scale * 1.4426950408889634 - 1.0) < 1e-6;
+  if (unit)
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<DP, NW, true>), dim3((unsigned)nblocks), dim3(NW * 64), 0, stream, a);
+  else
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<DP, NW, false>), dim3((unsigned)nblocks), dim3(NW * 64), 0, stream, a);
   return hipGetLastError();
 }
 

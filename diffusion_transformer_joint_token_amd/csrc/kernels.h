@@ -36,6 +36,7 @@ struct QkNormRopeArgs {
   int64_t qs[3], ks[3], qos[3], kos[3];
   int32_t B, S, H, Hk, D;
   float eps;
+  float q_scale;                 // extra factor on Q outputs
   double omega[kMaxPairs];       // frequency of channel pair p
   int32_t pair_axis[kMaxPairs];  // axis that owns pair p
 };

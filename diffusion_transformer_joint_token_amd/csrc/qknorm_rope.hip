@@ -137,7 +137,7 @@ __global__ __launch_bounds__(kThreads) void qknorm_rope_kernel(QkNormRopeArgs a)
       for (int i = 0; i < EPC; ++i) ss = fmaf(x[i], x[i], ss);
 #pragma unroll
       for (int m = LPH / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
-      const float inv = 1.0f / sqrtf(ss / (float)D + a.eps);
+      const float inv = 1.0f / sqrtf(ss / (float)D + a.eps) * (is_q ? a.q_scale : 1.0f);
       float y[EPC];
 #pragma unroll
       for (int i = 0; i < EPC; ++i) y[i] = x[i] * inv * (is_q ? wq[i] : wk[i]);

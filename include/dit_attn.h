@@ -122,6 +122,9 @@ int dit_attn_build_token_metadata(const uint8_t *image_pad_mask, int32_t seq_len
  *   y = x / sqrt(mean_d x_d^2 + eps) * w            (w: q_weight or k_weight)
  *   then for axis a owning channels [o_a, o_a + d_a), pair j turns
  *   (y[o_a+2j], y[o_a+2j+1]) by pos[s][a] * rope_theta^(-2j/d_a).
+ * Q outputs are then multiplied by q_scale (1 = plain); passing
+ * q_scale = log2(e) * softmax_scale folds the attention's softmax scale into Q
+ * with a single rounding (then call the attention with softmax_scale = ln 2).
  * V is not touched.  Arithmetic in fp32; outputs rounded to the dtype (RNE).
  *   q, k           device [B, S, H | H_kv, D] in dtype, strides q_strides/k_strides.
  *   q_out, k_out   device outputs (may alias q, k exactly), strides qo_/ko_strides.
@@ -129,7 +132,7 @@ int dit_attn_build_token_metadata(const uint8_t *image_pad_mask, int32_t seq_len
  *   pos_ids        device int32 [S][3] (the metadata's pos_ids; for the new
  *                  tokens of a cached step pass meta.pos_ids + 3 * prefix_len).
  *   n_axes         2 or 3; axes_dims host int32 [n_axes], each even, summing to D.
- *   rope_theta     rotary base (> 0).  eps >= 0.
+ *   rope_theta     rotary base (> 0).  eps >= 0.  q_scale finite, != 0.
  * Requirements: D % 8 == 0 (bf16) or D % 4 == 0 (f32), 8 <= D <= 128. */
 int dit_attn_qknorm_rope(const void *q, const void *k, void *q_out, void *k_out,
                          const void *q_weight, const void *k_weight,
@@ -137,7 +140,7 @@ int dit_attn_qknorm_rope(const void *q, const void *k, void *q_out, void *k_out,
                          const int64_t q_strides[3], const int64_t k_strides[3],
                          const int64_t qo_strides[3], const int64_t ko_strides[3],
                          const int32_t *pos_ids, int32_t n_axes, const int32_t *axes_dims,
-                         float rope_theta, float eps, int32_t dtype, void *stream);
+                         float rope_theta, float eps, float q_scale, int32_t dtype, void *stream);
 
 /* Masked softmax attention (QwenImage21Transformer2DModel API page, block-causal
  * attention; NucleusMoE-Image article section 6.3 for GQA):
@@ -150,7 +153,9 @@ int dit_attn_qknorm_rope(const void *q, const void *k, void *q_out, void *k_out,
  *                or NULL.
  *   meta         host struct; only kv_limit is read (may be NULL for FULL);
  *                meta->seq_len must equal S.
- *   softmax_scale  <= 0 selects 1/sqrt(D).
+ *   softmax_scale  <= 0 selects 1/sqrt(D).  With Q pre-multiplied by
+ *                  log2(e) * scale (dit_attn_qknorm_rope's q_scale), pass ln 2: the
+ *                  kernel then exponentiates the MFMA output directly.
  * bf16: QK^T and PV on bf16 MFMA with fp32 accumulation, P rounded to bf16 for
  * PV, O rounded once.  f32: fp32 throughout.  D <= 128, D % 8 == 0. */
 int dit_attn_forward(const void *q, const void *k, const void *v, void *o, float *lse,

@@ -76,9 +76,10 @@ def test_qknorm_rope_argument_errors():
     st = _s3(5120 * 4096, 4096, 128)
     axes = (ctypes.c_int32 * 3)(16, 56, 56)
 
-    def call(q=FAKE, D=128, axes_arr=axes, n_axes=3, dtype=0, strides=st, theta=1e4, eps=1e-6, H=32, Hk=32):
+    def call(q=FAKE, D=128, axes_arr=axes, n_axes=3, dtype=0, strides=st, theta=1e4, eps=1e-6, H=32, Hk=32,
+             q_scale=1.0):
         return f(q, FAKE, FAKE2, FAKE2, None, None, 2, 5120, H, Hk, D, strides, strides, strides, strides, FAKE,
-                 n_axes, axes_arr, theta, eps, dtype, None)
+                 n_axes, axes_arr, theta, eps, q_scale, dtype, None)
     assert call(q=None) == _lib.ERR_NULL
     assert call(dtype=5) == _lib.ERR_UNSUPPORTED
     assert call(D=136) == _lib.ERR_UNSUPPORTED
@@ -88,6 +89,8 @@ def test_qknorm_rope_argument_errors():
     assert call(n_axes=4) == _lib.ERR_SHAPE
     assert call(theta=0.0) == _lib.ERR_SHAPE
     assert call(eps=-1.0) == _lib.ERR_SHAPE
+    assert call(q_scale=0.0) == _lib.ERR_SHAPE
+    assert call(q_scale=float("inf")) == _lib.ERR_SHAPE
     assert call(H=0) == _lib.ERR_SHAPE
     assert call(q=FAKE + 2) == _lib.ERR_ALIGN
     assert call(strides=_s3(5120 * 4096, 4096, 132)) == _lib.ERR_ALIGN   # head stride 264 B

@@ -166,6 +166,11 @@ def test_qknorm_rope_small(dit, case):
     rk = oqr.qknorm_rope(d.vals["k"], d.vals["wk"], w.eps, md["pos_ids"], axes)
     assert_parity(to_host(qo), rq, dtype, "q'")
     assert_parity(to_host(ko), rk, dtype, "k'")
+    # q_scale multiplies Q' (before its single rounding) and leaves K' alone.
+    qs, ks2 = dit.qknorm_rope(q, k, m.pos_ids, axes, w.eps, wq, wk, q_scale=0.3)
+    torch.cuda.synchronize()
+    assert_parity(to_host(qs), 0.3 * rq, dtype, "q' x 0.3")
+    assert torch.equal(ks2, ko)
     # In place on strided views of one fused buffer gives the same bits.
     fused = torch.zeros(B, S, H + 2 * Hk + 1, D, dtype=q.dtype, device="cuda")
     fused[:, :, :H] = q
@@ -221,58 +226,78 @@ def _case_id(c):
         s[1] if s[0] == "T" else s[1] * s[2] * s[3] for s in c[4]), c[7])
 
 
+@pytest.mark.parametrize("prescaled", [False, True], ids=["plain", "prescaled"])
 @pytest.mark.parametrize("case", ATT_CASES, ids=_case_id)
-def test_attention_small_all_rows(dit, case):
+def test_attention_small_all_rows(dit, case, prescaled):
     """Synthetic Q', K', V straight into the attention entry points (no norm),
-    every output element and the lse checked."""
+    every output element and the lse checked.  "prescaled" hands the kernel
+    Q' x scale x log2(e) (rounded once to the dtype) with the scale argument
+    ln 2; the oracle then gets exactly those Q values divided back (float64)
+    with the default 1/sqrt(D) scale, which is the same attention."""
     B, H, Hk, D, layout, mode, dtype, P = case
     w = wl.small_workload("a", B, H, Hk, D, layout, (D,), dtype=dtype, seed=D + P, prefix_len=P)
-    _say("attention %s" % _case_id(case))
+    _say("attention %s %s" % (_case_id(case), "prescaled" if prescaled else "plain"))
     d = wl.draw(w)
     mask, shapes = wl.sequence_inputs(w)
     md = ometa.build_token_metadata(mask, shapes)
     m = _meta_gpu(dit, mask, shapes, "centered_fhw")
-    q, k, v = (to_device(d.bits[n], dtype) for n in ("q", "k", "v"))
+    q_vals, q_bits, scale = d.vals["q"], d.bits["q"], None
+    if prescaled:
+        c = dit.prescaled_q_factor(D)
+        if dtype == "bf16":
+            q_bits = wl.bf16_round_bits((d.vals["q"] * c).astype(np.float32))
+            q_vals = wl.bf16_bits_to_f64(q_bits) / c
+        else:
+            q_bits = (d.vals["q"] * c).astype(np.float32)
+            q_vals = q_bits.astype(np.float64) / c
+        scale = dit.LN2
+    q = to_device(q_bits, dtype)
+    k, v = (to_device(d.bits[n], dtype) for n in ("k", "v"))
     if P:
         kc, vc = to_device(d.bits["k_cache"], dtype), to_device(d.bits["v_cache"], dtype)
-        o, lse = dit.forward_cached(q, kc, vc, k, v, mode, m, return_lse=True)
+        o, lse = dit.forward_cached(q, kc, vc, k, v, mode, m, softmax_scale=scale, return_lse=True)
         k_all = np.concatenate([d.vals["k_cache"], d.vals["k"]], axis=1)
         v_all = np.concatenate([d.vals["v_cache"], d.vals["v"]], axis=1)
     else:
-        o, lse = dit.forward(q, k, v, mode, m, return_lse=True)
+        o, lse = dit.forward(q, k, v, mode, m, softmax_scale=scale, return_lse=True)
         k_all, v_all = d.vals["k"], d.vals["v"]
     torch.cuda.synchronize()
-    ro, rl = oatt.attention(d.vals["q"], k_all, v_all, md["image_ids"], mode, q_offset=P)
+    ro, rl = oatt.attention(q_vals, k_all, v_all, md["image_ids"], mode, q_offset=P)
     assert_parity(to_host(o), ro, dtype, "O")
     assert_parity(lse.cpu().double().numpy(), rl, "f32", "lse", atol=1e-2 if dtype == "bf16" else 1e-5)
 
 
-def _pipeline(dit, w: wl.Workload, d: wl.Drawn, m):
-    """K2 then K3 on the GPU for workload w; returns (o, lse, q', k')."""
+def _pipeline(dit, w: wl.Workload, d: wl.Drawn, m, prescaled: bool):
+    """K2 then K3 on the GPU for workload w; returns (o, lse, q', k').  With
+    prescaled, K2 folds the softmax scale and log2(e) into Q' and the
+    attention runs with scale ln 2 (what the benchmark times)."""
     P = w.prefix_len
     q, k, v = (to_device(d.bits[n], w.dtype) for n in ("q", "k", "v"))
     wq, wk = to_device(d.bits["wq"], w.dtype), to_device(d.bits["wk"], w.dtype)
-    qp, kp = dit.qknorm_rope(q, k, m.pos_ids[P:], w.axes, w.eps, wq, wk)
+    q_scale = dit.prescaled_q_factor(w.head_dim) if prescaled else 1.0
+    scale = dit.LN2 if prescaled else None
+    qp, kp = dit.qknorm_rope(q, k, m.pos_ids[P:], w.axes, w.eps, wq, wk, q_scale=q_scale)
     if P:
         kc, vc = to_device(d.bits["k_cache"], w.dtype), to_device(d.bits["v_cache"], w.dtype)
-        o, lse = dit.forward_cached(qp, kc, vc, kp, v, w.mask_mode, m, return_lse=True)
+        o, lse = dit.forward_cached(qp, kc, vc, kp, v, w.mask_mode, m, softmax_scale=scale, return_lse=True)
     else:
-        o, lse = dit.forward(qp, kp, v, w.mask_mode, m, return_lse=True)
+        o, lse = dit.forward(qp, kp, v, w.mask_mode, m, softmax_scale=scale, return_lse=True)
     torch.cuda.synchronize()
     return o, lse, qp, kp
 
 
+@pytest.mark.parametrize("prescaled", [True, False], ids=["prescaled", "plain"])
 @pytest.mark.parametrize("name", list(wl.WORKLOADS))
-def test_pipeline_workloads(dit, name):
+def test_pipeline_workloads(dit, name, prescaled):
     """The whole step (metadata -> norm+rope -> attention) at full size; the
     oracle computes sampled query rows (all rows for the tiny workload)."""
     w = wl.WORKLOADS[name]
-    _say("pipeline %s" % name)
+    _say("pipeline %s %s" % (name, "prescaled" if prescaled else "plain"))
     d = wl.draw(w)
     mask, shapes = wl.sequence_inputs(w)
     md = ometa.build_token_metadata(mask, shapes, w.pos_mode)
     m = _meta_gpu(dit, mask, shapes, w.pos_mode)
-    o, lse, _, _ = _pipeline(dit, w, d, m)
+    o, lse, _, _ = _pipeline(dit, w, d, m, prescaled)
     P = w.prefix_len
     rows = np.arange(w.n_new) if w.n_new <= 64 else sample_rows(w)
     pos = md["pos_ids"][P:]
