@@ -12,10 +12,17 @@
 //                Lumina 2D grid (NucleusMoE-Image article section 6.3;
 //                Lumina-Next DiT article sections 1 and 4).
 //
-// One work-group of 1024 threads walks the sequence in chunks, ranking image
-// tokens with a block-wide prefix sum; the work is a few integer operations
-// per token, so the launch itself dominates.  Data errors (count mismatch,
-// split block, text under 2D positions) go to a device status word.
+// One work-group of 1024 threads.  Per pass each wave owns a contiguous
+// segment of 64 * TPT tokens: it counts its image tokens, a block-wide scan
+// over the 16 wave counts gives each segment its starting rank, and the wave
+// then walks its segment 64 tokens at a time with lane = token, ranking image
+// tokens with a ballot and mbcnt, so every load and store is coalesced.  A
+// block's first and last tokens are the unique tokens holding its first and
+// last ranks, so they are recorded without atomics; an image token's key bound
+// is its position minus its rank in the block plus the block size, exact
+// whenever the block is contiguous, which the first/last check verifies.
+// Data errors (count mismatch, split block, text under 2D positions) go to a
+// device status word.
 
 #include "device_common.h"
 #include "kernels.h"
@@ -26,15 +33,13 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
+constexpr int TPT = 8;                  // 64-token groups per wave and pass
+constexpr int kSeg = 64 * TPT;          // tokens per wave and pass
+constexpr int kPass = kWaves * kSeg;    // tokens per pass
 
-__device__ __forceinline__ int wave_inclusive_scan(int x) {
-  const int lane = __lane_id();
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    int y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
-  return x;
+// Number of set bits of `bits` in the lanes below this one.
+__device__ __forceinline__ int lanes_below(uint64_t bits) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(bits >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bits, 0));
 }
 
 __global__ __launch_bounds__(kThreads) void token_meta_kernel(const uint8_t* __restrict__ mask,
@@ -46,7 +51,8 @@ __global__ __launch_bounds__(kThreads) void token_meta_kernel(const uint8_t* __r
   __shared__ int s_first[kMaxImages];
   __shared__ int s_last[kMaxImages];
   __shared__ int s_cum[kMaxImages + 1];
-  __shared__ int s_wave_tot[kWaves];
+  __shared__ int s_shape[kMaxImages][4];  // height, width, height * width, frame offset
+  __shared__ int s_wave_cnt[kWaves];
   __shared__ int s_carry;
   __shared__ int s_bad;
 
@@ -57,90 +63,115 @@ __global__ __launch_bounds__(kThreads) void token_meta_kernel(const uint8_t* __r
   const int S = a.seq_len;
 
   if (tid < kMaxImages) {
-    s_first[tid] = 0x7fffffff;
+    s_first[tid] = -1;
     s_last[tid] = -1;
   }
   if (tid <= n_img) s_cum[tid] = a.cum[tid];
+  if (tid < n_img) {  // per-block constants, read from LDS in the token loop
+    s_shape[tid][0] = a.shape[tid][1];
+    s_shape[tid][1] = a.shape[tid][2];
+    s_shape[tid][2] = a.shape[tid][1] * a.shape[tid][2];
+    s_shape[tid][3] = a.frame_off[tid];
+  }
   if (tid == 0) {
     s_carry = 0;
     s_bad = 0;
   }
   __syncthreads();
   const int total_expected = s_cum[n_img];
+  int bad = 0;
 
-  for (int base = 0; base < S; base += kThreads) {
-    const int s = base + tid;
-    const int m = (s < S && mask[s] != 0) ? 1 : 0;
-    int incl = wave_inclusive_scan(m);
-    if (lane == 63) s_wave_tot[wave] = incl;
+  for (int base = 0; base < S; base += kPass) {
+    const int seg = base + wave * kSeg;
+    // Image tokens of this wave's segment.
+    int cnt = 0;
+#pragma unroll
+    for (int it = 0; it < TPT; ++it) {
+      const int s = seg + it * 64 + lane;
+      cnt += (s < S && mask[s] != 0) ? 1 : 0;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off, 64);
+    if (lane == 0) s_wave_cnt[wave] = cnt;
     __syncthreads();
-    int wave_off = 0;
-    for (int w = 0; w < wave; ++w) wave_off += s_wave_tot[w];
-    const int carry = s_carry;
-    incl += wave_off + carry;  // image tokens in [0, s]
-    if (s < S) {
-      int id = -1;
-      int p0 = 0, p1 = 0, p2 = 0;
-      if (m) {
-        const int r = incl - 1;  // rank of this image token
-        if (r >= total_expected) {
-          s_bad = 1;
-        } else {
-          // block b with cum[b] <= r < cum[b + 1]
-          int lo = 0, hi = n_img - 1;
-          while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (s_cum[mid] <= r) lo = mid; else hi = mid - 1;
-          }
-          id = lo;
-          const int local = r - s_cum[id];
-          atomicMin(&s_first[id], s);
-          atomicMax(&s_last[id], s);
-          const int F = a.shape[id][0], Hh = a.shape[id][1], W = a.shape[id][2];
-          (void)F;
-          const int f = local / (Hh * W);
-          const int h = (local / W) % Hh;
-          const int w = local % W;
-          if (a.pos_mode == 0) {
-            p0 = a.frame_off[id] + f;
-            p1 = h - Hh / 2;
-            p2 = w - W / 2;
-          } else {
-            p0 = h;
-            p1 = w;
-            p2 = 0;
-          }
-        }
-      } else {
-        if (a.pos_mode == 0) {
-          const int t = s - incl;  // text tokens before s (s itself is text)
-          p0 = p1 = p2 = a.max_vid + t;
-        } else {
-          s_bad = 1;
-        }
+    int r0 = s_carry;  // rank of the first image token of this segment
+    for (int w = 0; w < wave; ++w) r0 += s_wave_cnt[w];
+    int blk = 0;
+    {
+      int lo = 0, hi = n_img > 0 ? n_img - 1 : 0;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_cum[mid] <= r0) lo = mid; else hi = mid - 1;
       }
-      image_ids[s] = id;
-      pos[3 * s + 0] = p0;
-      pos[3 * s + 1] = p1;
-      pos[3 * s + 2] = p2;
+      blk = lo;
+    }
+    bool m[TPT];
+#pragma unroll
+    for (int it = 0; it < TPT; ++it) {
+      const int s = seg + it * 64 + lane;
+      m[it] = s < S && mask[s] != 0;
+    }
+#pragma unroll
+    for (int it = 0; it < TPT; ++it) {
+      const int s = seg + it * 64 + lane;
+      const uint64_t bits = __ballot(m[it]);
+      const int r = r0 + lanes_below(bits);  // image tokens before s
+      if (s < S) {
+        int id = -1, p0 = 0, p1 = 0, p2 = 0, lim = s + 1;
+        if (m[it]) {
+          if (r >= total_expected) {
+            bad = 1;
+          } else {
+            int b = blk;
+            while (s_cum[b + 1] <= r) ++b;
+            id = b;
+            const int count = s_cum[b + 1] - s_cum[b];
+            const int local = r - s_cum[b];
+            if (local == 0) s_first[b] = s;
+            if (local == count - 1) s_last[b] = s;
+            // One past the block's last token, if the block is contiguous
+            // (checked below through its first and last tokens).
+            lim = s - local + count;
+            const int Hh = s_shape[b][0], W = s_shape[b][1];
+            const int f = local / s_shape[b][2];
+            const int h = (local / W) % Hh;
+            const int w = local % W;
+            if (a.pos_mode == 0) {
+              p0 = s_shape[b][3] + f;
+              p1 = h - Hh / 2;
+              p2 = w - W / 2;
+            } else {
+              p0 = h;
+              p1 = w;
+            }
+          }
+        } else if (a.pos_mode == 0) {
+          p0 = p1 = p2 = a.max_vid + (s - r);  // s - r = text tokens before s
+        } else {
+          bad = 1;
+        }
+        image_ids[s] = id;
+        pos[3 * s + 0] = p0;
+        pos[3 * s + 1] = p1;
+        pos[3 * s + 2] = p2;
+        kv_limit[s] = lim;
+        target[s] = (id >= 0 && id == n_img - 1) ? 1 : 0;
+      }
+      r0 += __builtin_popcountll(bits);
+      while (n_img > 0 && blk < n_img - 1 && s_cum[blk + 1] <= r0) ++blk;
     }
     __syncthreads();
-    if (tid == kThreads - 1) s_carry = incl;
+    if (tid == kThreads - 1) s_carry = r0;
     __syncthreads();
   }
-
+  if (bad) s_bad = 1;
+  __syncthreads();
   if (tid == 0 && s_carry != total_expected) s_bad = 1;
   if (tid < n_img) {
-    const long long span = (long long)s_last[tid] - (long long)s_first[tid] + 1;
-    if (span != (long long)(s_cum[tid + 1] - s_cum[tid])) s_bad = 1;
+    const int first = s_first[tid], last = s_last[tid];
+    if (first < 0 || last < 0 || last - first + 1 != s_cum[tid + 1] - s_cum[tid]) s_bad = 1;
   }
   __syncthreads();
-
-  for (int s = tid; s < S; s += kThreads) {
-    const int id = image_ids[s];  // written by this same thread above
-    kv_limit[s] = (id < 0) ? s + 1 : s_last[id] + 1;
-    target[s] = (id >= 0 && id == n_img - 1) ? 1 : 0;
-  }
   if (tid == 0) status[0] = s_bad ? 5 : 0;
 }
 
