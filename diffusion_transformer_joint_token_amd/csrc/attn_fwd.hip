@@ -22,12 +22,14 @@
 //    ds_read_b64_tr_b16, whose 16-lane transpose delivers 4 consecutive keys of
 //    one head channel per lane in exactly the key order of the accumulator.
 //  * K and V tiles move global -> LDS with direct 16-byte LDS loads (no VGPR
-//    staging), double-buffered; 16-byte chunks are XOR-swizzled per row so both
-//    the K reads (16 rows, same chunk) and the transposed V reads (4 rows x 4
-//    chunks) hit distinct banks.
-//  * Softmax in the exp2 domain with the scale folded into one FMA; the running
-//    max is only moved when a row's new maximum exceeds it by more than 8
-//    (log2 units), so O is rarely rescaled and probabilities stay <= 2^8.
+//    staging) into two K and two V stages; each stage is refilled right after
+//    the barrier that ends its last read, so a tile has 1.5 iterations to land
+//    (two barriers per iteration, waits counted in vector-memory instructions).
+//    16-byte chunks are XOR-swizzled per row so both the K reads (16 rows, same
+//    chunk) and the transposed V reads (4 rows x 4 chunks) hit distinct banks.
+//  * Softmax in the exp2 domain; the running max is only moved when a row's
+//    new maximum exceeds it by more than 8 (log2 units), so O is rarely
+//    rescaled and probabilities stay <= 2^8.
 //  * Work-groups are ordered heaviest query tile first and mapped so that all
 //    query tiles of one (batch, head) share an XCD (and its L2).
 
@@ -63,6 +65,11 @@ __device__ __forceinline__ void map_block(int id, int nblocks, int n_qtiles, int
 // Buffer resource word 3 for untyped 32-bit accesses on gfx9-class parts.
 constexpr int kRsrcWord3 = 0x00020000;
 
+// s_waitcnt immediate (gfx9 layout): vmcnt in bits [3:0] and [15:14], expcnt
+// in [6:4] (7: no wait), lgkmcnt in [11:8].  Issued through the builtin so the
+// compiler's own wait insertion knows what has already been waited for.
+constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
+
 // acc + lo + hi of a packed bf16 pair, in one v_dot2 against (1, 1).
 __device__ __forceinline__ float add_bf16_pair(uint32_t pair, float acc) {
   const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
@@ -77,7 +84,9 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, char* dst, in
 
 // UNIT: Q already carries softmax_scale * log2(e) (scale argument ln 2), so the
 // MFMA output is the exponent itself.
-template <int DP, int NW, bool UNIT>
+// ALIGNED: the cache length P is a multiple of the key tile, so no tile mixes
+// cached and new keys and every tile load comes from one source.
+template <int DP, int NW, bool UNIT, bool ALIGNED>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   static_assert(DP % 32 == 0 && DP <= 128, "padded head dim");
   constexpr int KSTEPS = DP / 16;  // QK^T contraction steps
@@ -133,6 +142,15 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
     }
   }
 
+  // Key tiles this work-group visits (the largest bound of its waves).  Bare
+  // barrier: only the s_lim stores must have landed, not the Q loads.
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+  __builtin_amdgcn_s_barrier();
+  int wg_lim = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) wg_lim = max(wg_lim, s_lim[w]);
+  const int n_tiles = (wg_lim + kTileN - 1) / kTileN;
+
   // Global -> LDS loader on buffer resources (one per K/V source), so a
   // tile costs one address add per load.  Position p = 64*(i*NW + wave) + lane
   // of a tile is row p/16, physical chunk p%16, holding logical chunk
@@ -149,43 +167,53 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   const __amdgpu_buffer_rsrc_t rs_vc = __builtin_amdgcn_make_buffer_rsrc((void*)vc, 0, P > 0 ? (P - 1) * rvc + rowbytes : 0, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rs_kn = __builtin_amdgcn_make_buffer_rsrc((void*)kn, 0, (a.Snew - 1) * rkn + rowbytes, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rs_vn = __builtin_amdgcn_make_buffer_rsrc((void*)vn, 0, (a.Snew - 1) * rvn + rowbytes, kRsrcWord3);
+  // Load i of a tile covers rows lr + 4*NW*i (lr = 4*wave + lane/16), 16
+  // lanes per row.  With NW a multiple of 4 the row swizzle of lr + 4*NW*i
+  // equals that of lr, so one per-lane byte offset per source serves all
+  // loads; the wave index is read as a scalar so the LDS destinations stay in
+  // scalar registers.  Lanes whose chunk lies beyond the padded head dim get
+  // an offset past every extent (bit 31 set; the host keeps extents below
+  // 2^31), so they read zeros without fetching and every load instruction
+  // runs unmasked.
+  static_assert(NW % 4 == 0, "loader assumes whole swizzle periods per load");
   const int dchunks = a.D / 8;
-  int lrow[LOADS], lcol[LOADS];
-  bool lact[LOADS];
-#pragma unroll
-  for (int i = 0; i < LOADS; ++i) {
-    const int p = 64 * (i * NW + wave) + lane;
-    lrow[i] = p >> 4;
-    const int c = (p & 15) ^ swz(lrow[i]);
-    lact[i] = c < CHUNKS;
-    lcol[i] = 16 * (c < dchunks ? c : 0);  // padding channels: any finite data (Q is zero there)
-  }
-  // One source: keys [k0, k0 + 64) all cached (k0 + 64 <= P) or all new (k0 >= P).
-  // Otherwise (the tile holding key P) each lane picks its own source.
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int lr = 4 * wv + (lane >> 4);
+  const int lc = (lane & 15) ^ swz(lr);
+  const uint32_t lcol = 16 * (lc < dchunks ? lc : 0);  // padding channels: any finite data (Q is zero there)
+  const uint32_t loob = lc < CHUNKS ? 0u : 0x80000000u;
+  const uint32_t vo_kc = (uint32_t)(lr * rkc) + lcol + loob, vo_vc = (uint32_t)(lr * rvc) + lcol + loob;
+  const uint32_t vo_kn = (uint32_t)(lr * rkn) + lcol + loob, vo_vn = (uint32_t)(lr * rvn) + lcol + loob;
+  constexpr int kSlab = 4 * NW;  // rows per load instruction and work-group
+  // A tile past the work-group's last one is still issued, through a resource
+  // of extent zero (every lane reads zeros, nothing is fetched), so that each
+  // issue is exactly LOADS unmasked instructions per wave and the waits below
+  // can count them.  A tile holds keys of one source (all cached, k0 + 64 <= P,
+  // or all new, k0 >= P; always so when P is a multiple of 64) or, only when
+  // P is not, is the one tile holding key P, where each lane picks its source.
+  const __amdgpu_buffer_rsrc_t rs_null = __builtin_amdgcn_make_buffer_rsrc((void*)kn, 0, 0, kRsrcWord3);
   auto issue = [&](int t, char* dst, bool is_k) {
-    const int k0 = t * kTileN;
-    const __amdgpu_buffer_rsrc_t rc = is_k ? rs_kc : rs_vc;
-    const __amdgpu_buffer_rsrc_t rn = is_k ? rs_kn : rs_vn;
-    const int sc = is_k ? rkc : rvc;
-    const int sn = is_k ? rkn : rvn;
-    if (k0 + kTileN <= P) {
+    const bool live = t < n_tiles;
+    const int k0 = live ? t * kTileN : 0;
+    char* d0 = dst + 1024 * wv;
+    if (ALIGNED || k0 + kTileN <= P || k0 >= P) {
+      const bool cached = k0 < P;
+      const __amdgpu_buffer_rsrc_t r = !live ? rs_null : cached ? (is_k ? rs_kc : rs_vc) : (is_k ? rs_kn : rs_vn);
+      const int st = cached ? (is_k ? rkc : rvc) : (is_k ? rkn : rvn);
+      const uint32_t o = cached ? (is_k ? vo_kc : vo_vc) : (is_k ? vo_kn : vo_vn);
+      const int r0 = cached ? k0 : k0 - P;
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i)
-        if (lact[i])
-          dma16(rc, dst + 1024 * (i * NW + wave), (k0 + lrow[i]) * sc + lcol[i]);
-    } else if (k0 >= P) {
-#pragma unroll
-      for (int i = 0; i < LOADS; ++i)
-        if (lact[i])
-          dma16(rn, dst + 1024 * (i * NW + wave), (k0 - P + lrow[i]) * sn + lcol[i]);
+      for (int i = 0; i < LOADS; ++i) dma16(r, d0 + 1024 * NW * i, (int)(o + (uint32_t)((r0 + kSlab * i) * st)));
     } else {
+      const __amdgpu_buffer_rsrc_t rc = is_k ? rs_kc : rs_vc;
+      const __amdgpu_buffer_rsrc_t rn = is_k ? rs_kn : rs_vn;
+      const int sc = is_k ? rkc : rvc, sn = is_k ? rkn : rvn;
+      const uint32_t oc = is_k ? vo_kc : vo_vc, on = is_k ? vo_kn : vo_vn;
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
-        const int key = k0 + lrow[i];
-        if (lact[i] && key < P)
-          dma16(rc, dst + 1024 * (i * NW + wave), key * sc + lcol[i]);
-        if (lact[i] && key >= P)
-          dma16(rn, dst + 1024 * (i * NW + wave), (key - P) * sn + lcol[i]);
+        const int key = k0 + kSlab * i + lr;
+        if (key < P) dma16(rc, d0 + 1024 * NW * i, (int)(oc + (uint32_t)((k0 + kSlab * i) * sc)));
+        if (key >= P) dma16(rn, d0 + 1024 * NW * i, (int)(on + (uint32_t)((k0 - P + kSlab * i) * sn)));
       }
     }
   };
@@ -321,20 +349,21 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
     }
   };
 
-  // One iteration: S(t) (masked, shifted, its max mx_cur) is in s_cur, K(t+1)
-  // and V(t) are in LDS.  Softmax of tile t runs interleaved with the QK^T
-  // MFMAs of tile t+1, then PV of tile t with the row max of tile t+1.
+  // Iteration t, phase 1: S(t) (masked, its max mx_cur) is in s_cur and K(t+1)
+  // is in LDS; the softmax of tile t runs interleaved with the QK^T MFMAs of
+  // tile t+1.  Phase 2: V(t) is in LDS; PV of tile t runs interleaved with the
+  // mask and row max of tile t+1.
   f32x16 s_cur[2], s_nxt[2];
+  bf16x8 pop[2][2];
   float mx_cur = -INFINITY;
-  auto step = [&](int t, const char* k_next, const char* v_cur) {
+  auto phase1 = [&](int t, const char* k_next) {
     const int k0 = t * kTileN;
     if (k0 >= wlim_max) return;  // wave-uniform: nothing allowed from here on
     update(mx_cur, s_cur);
-    bf16x8 pop[2][2];
     const int k1 = k0 + kTileN;
-    const bool has_next = (t + 1) * kTileN < wlim_max && k1 < Sk;
+    const bool has_next = k1 < wlim_max && k1 < Sk;
+    softmax(s_cur, pop);
     if (has_next) {
-      softmax(s_cur, pop);
       qk(k_next, s_nxt);
       __builtin_amdgcn_sched_group_barrier(0x100, PF_K, 0);  // DS read (K operand) ahead
 #pragma unroll
@@ -348,6 +377,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
       }
+    }
+  };
+  auto phase2 = [&](int t, const char* v_cur) {
+    const int k0 = t * kTileN;
+    if (k0 >= wlim_max) return;
+    const int k1 = k0 + kTileN;
+    const bool has_next = k1 < wlim_max && k1 < Sk;
+    if (has_next) {
       if (k1 + kTileN > wlim_min) {
         pv(v_cur, pop);
         mask(t + 1, s_nxt);
@@ -371,41 +408,64 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
     } else {
-      softmax(s_cur, pop);
       pv(v_cur, pop);
     }
   };
 
-  __syncthreads();  // s_lim
-  int wg_lim = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) wg_lim = max(wg_lim, s_lim[w]);
-  const int n_tiles = (wg_lim + kTileN - 1) / kTileN;
 
-  // Prologue: K(0), V(0), K(1) in flight; S(0) once they land.
+  // Load schedule (two K and two V stages).  A stage is refilled right after
+  // the barrier that ends its last read: K(t+3) at the middle of iteration t
+  // (after QK^T(t+1) read K(t+1)), V(t+2) at the top of iteration t+1 (after
+  // PV(t) read V(t)).  Each tile thus has 1.5 iterations to land.  Every issue
+  // is exactly LOADS vector-memory instructions per wave (at least LOADS on a
+  // tile that mixes cached and new keys) and loads complete in order, so at
+  // each wait "at most 2*LOADS outstanding" means the tile issued two issues
+  // earlier has landed:
+  //   top of t:  K(t+1) | V(t), K(t+2)     -> K(t+1) in LDS
+  //   mid of t:  V(t)   | K(t+2), V(t+1)   -> V(t) in LDS
+  // Each wave waits for its own loads and its own LDS reads, then a bare
+  // barrier (a workgroup fence would drain every load in flight) makes the
+  // tile whole and the stage about to be refilled unread.
+  auto wait_tile = [&]() {
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * LOADS, 0));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  // Prologue: K(0), K(1), V(0); S(0) once they land; then K(2).
   issue(0, sK0, true);
+  issue(1, sK1, true);
   issue(0, sV0, false);
-  if (n_tiles > 1) issue(1, sK1, true);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
   qk(sK0, s_cur);
   if (kTileN > wlim_min) mask(0, s_cur);
   mx_cur = rowmax(s_cur);
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+  __builtin_amdgcn_s_barrier();  // every wave is done with K(0)
+  asm volatile("" ::: "memory");
+  issue(2, sK0, true);
 
   // Stages are named statically, two iterations per trip.
   for (int t = 0; t < n_tiles; t += 2) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (t + 2 < n_tiles) issue(t + 2, sK0, true);
-    if (t + 1 < n_tiles) issue(t + 1, sV1, false);
-    step(t, sK1, sV0);
+    wait_tile();  // K(t+1) in sK1; sV1 (V(t-1)) read by every wave
+    issue(t + 1, sV1, false);
+    phase1(t, sK1);
+    wait_tile();  // V(t) in sV0; sK1 (K(t+1)) read by every wave
+    issue(t + 3, sK1, true);
+    phase2(t, sV0);
     if (t + 1 >= n_tiles) break;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (t + 3 < n_tiles) issue(t + 3, sK1, true);
-    if (t + 2 < n_tiles) issue(t + 2, sV0, false);
-    step(t + 1, sK0, sV1);
+    wait_tile();  // K(t+2) in sK0; sV0 (V(t)) read by every wave
+    issue(t + 2, sV0, false);
+    phase1(t + 1, sK0);
+    wait_tile();  // V(t+1) in sV1; sK0 (K(t+2)) read by every wave
+    issue(t + 4, sK0, true);
+    phase2(t + 1, sV1);
   }
+  // Tiles past the last one were issued too: drain before the work-group's
+  // LDS can be handed to another.
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
 
   // Normalise and store: lane holds query (lane & 31), channels
   // 32*mb + 8*(i/4) + 4*g + (i%4).
@@ -522,10 +582,16 @@ hipError_t launch_bf16(const AttnArgs& a, hipStream_t stream) {
   const long long nblocks = (long long)n_qtiles * a.B * a.H;
   // Q pre-scaled by scale * log2(e): the scale argument is ln 2 (to rounding).
   const bool unit = std::fabs((double)a.scale * 1.4426950408889634 - 1.0) < 1e-6;
-  if (unit)
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<DP, NW, true>), dim3((unsigned)nblocks), dim3(NW * 64), 0, stream, a);
+  const bool aligned = a.P % 64 == 0;
+  const dim3 grid((unsigned)nblocks), block(NW * 64);
+  if (unit && aligned)
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<DP, NW, true, true>), grid, block, 0, stream, a);
+  else if (unit)
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<DP, NW, true, false>), grid, block, 0, stream, a);
+  else if (aligned)
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<DP, NW, false, true>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<DP, NW, false>), dim3((unsigned)nblocks), dim3(NW * 64), 0, stream, a);
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<DP, NW, false, false>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
