@@ -76,6 +76,14 @@ __device__ __forceinline__ float add_bf16_pair(uint32_t pair, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), one, acc, false);
 }
 
+// Value selects: a conditional between two captured variables would select
+// their addresses, which keeps a lambda's captures in private memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t pick(bool c, __amdgpu_buffer_rsrc_t x, __amdgpu_buffer_rsrc_t y) {
+  return c ? x : y;
+}
+__device__ __forceinline__ int pick(bool c, int x, int y) { return c ? x : y; }
+__device__ __forceinline__ uint32_t pick(bool c, uint32_t x, uint32_t y) { return c ? x : y; }
+
 // 16 bytes per lane from a buffer resource straight into LDS (lane i lands at
 // dst + 16 i); an offset past the resource's extent reads as zeros.
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, char* dst, int voffset) {
@@ -192,23 +200,24 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   // or all new, k0 >= P; always so when P is a multiple of 64) or, only when
   // P is not, is the one tile holding key P, where each lane picks its source.
   const __amdgpu_buffer_rsrc_t rs_null = __builtin_amdgcn_make_buffer_rsrc((void*)kn, 0, 0, kRsrcWord3);
-  auto issue = [&](int t, char* dst, bool is_k) {
+  auto issue = [&](int t, char* dst, bool is_k) __attribute__((always_inline)) {
     const bool live = t < n_tiles;
     const int k0 = live ? t * kTileN : 0;
     char* d0 = dst + 1024 * wv;
     if (ALIGNED || k0 + kTileN <= P || k0 >= P) {
       const bool cached = k0 < P;
-      const __amdgpu_buffer_rsrc_t r = !live ? rs_null : cached ? (is_k ? rs_kc : rs_vc) : (is_k ? rs_kn : rs_vn);
-      const int st = cached ? (is_k ? rkc : rvc) : (is_k ? rkn : rvn);
-      const uint32_t o = cached ? (is_k ? vo_kc : vo_vc) : (is_k ? vo_kn : vo_vn);
+      const __amdgpu_buffer_rsrc_t r =
+          pick(live, pick(cached, pick(is_k, rs_kc, rs_vc), pick(is_k, rs_kn, rs_vn)), rs_null);
+      const int st = pick(cached, pick(is_k, rkc, rvc), pick(is_k, rkn, rvn));
+      const uint32_t o = pick(cached, pick(is_k, vo_kc, vo_vc), pick(is_k, vo_kn, vo_vn));
       const int r0 = cached ? k0 : k0 - P;
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) dma16(r, d0 + 1024 * NW * i, (int)(o + (uint32_t)((r0 + kSlab * i) * st)));
     } else {
-      const __amdgpu_buffer_rsrc_t rc = is_k ? rs_kc : rs_vc;
-      const __amdgpu_buffer_rsrc_t rn = is_k ? rs_kn : rs_vn;
-      const int sc = is_k ? rkc : rvc, sn = is_k ? rkn : rvn;
-      const uint32_t oc = is_k ? vo_kc : vo_vc, on = is_k ? vo_kn : vo_vn;
+      const __amdgpu_buffer_rsrc_t rc = pick(is_k, rs_kc, rs_vc);
+      const __amdgpu_buffer_rsrc_t rn = pick(is_k, rs_kn, rs_vn);
+      const int sc = pick(is_k, rkc, rvc), sn = pick(is_k, rkn, rvn);
+      const uint32_t oc = pick(is_k, vo_kc, vo_vc), on = pick(is_k, vo_kn, vo_vn);
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
         const int key = k0 + kSlab * i + lr;
@@ -256,7 +265,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   float l_part = 0.f;  // this lane's share of the row sum
 
   // S^T (logits minus the offset, logit units) for the 64 keys of a K stage.
-  auto qk = [&](const char* kt, f32x16 (&sacc)[2]) {
+  auto qk = [&](const char* kt, f32x16 (&sacc)[2]) __attribute__((always_inline)) {
     const float init = -m_off * ic2;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -272,7 +281,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
     }
   };
   // Mask keys >= this row's bound (only tiles that reach past a wave's smallest bound).
-  auto mask = [&](int t, f32x16 (&sacc)[2]) {
+  auto mask = [&](int t, f32x16 (&sacc)[2]) __attribute__((always_inline)) {
     const int k0 = t * kTileN;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -282,7 +291,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
         if (key >= lim) sacc[kb][i] = -INFINITY;
       }
   };
-  auto rowmax = [&](const f32x16 (&sacc)[2]) {
+  auto rowmax = [&](const f32x16 (&sacc)[2]) __attribute__((always_inline)) {
     float mx = sacc[0][0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[0][i]);
@@ -293,7 +302,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   // mx: max of the tile's shifted logits (logit units).  Rows that grew past
   // the threshold (or see their first tile) move the offset to the tile max,
   // rescale O and l, and shift the tile's logits to the new offset.
-  auto update = [&](float mx, f32x16 (&sacc)[2]) {
+  auto update = [&](float mx, f32x16 (&sacc)[2]) __attribute__((always_inline)) {
     const bool grow = mx > -INFINITY && (fresh || mx * c2 > kLazyRescale);
     if (__any(grow)) {
       const float d = grow ? mx : 0.f;
@@ -308,7 +317,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
     fresh = false;
   };
   // P = exp2(c2 * S) as bf16 B operands; row sums from the same bf16 values.
-  auto softmax = [&](const f32x16 (&sacc)[2], bf16x8 (&pop)[2][2]) {
+  auto softmax = [&](const f32x16 (&sacc)[2], bf16x8 (&pop)[2][2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -328,7 +337,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   // V(t) are in LDS.  Softmax of tile t runs interleaved with the QK^T MFMAs of
   // tile t+1, then PV of tile t interleaved with the row max of tile t+1.
   // O^T += V^T P^T for the 64 keys of a V stage.
-  auto pv = [&](const char* vt, const bf16x8 (&pop)[2][2]) {
+  auto pv = [&](const char* vt, const bf16x8 (&pop)[2][2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -353,10 +362,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   // is in LDS; the softmax of tile t runs interleaved with the QK^T MFMAs of
   // tile t+1.  Phase 2: V(t) is in LDS; PV of tile t runs interleaved with the
   // mask and row max of tile t+1.
-  f32x16 s_cur[2], s_nxt[2];
+  // Two S buffers alternate roles across the unrolled iteration pair (tile t
+  // even: S(t) in sA, S(t+1) into sB; odd: the reverse), so no copies.
+  f32x16 sA[2], sB[2];
   bf16x8 pop[2][2];
   float mx_cur = -INFINITY;
-  auto phase1 = [&](int t, const char* k_next) {
+  auto phase1 = [&](int t, const char* k_next, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2]) __attribute__((always_inline)) {
     const int k0 = t * kTileN;
     if (k0 >= wlim_max) return;  // wave-uniform: nothing allowed from here on
     update(mx_cur, s_cur);
@@ -379,7 +390,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
       }
     }
   };
-  auto phase2 = [&](int t, const char* v_cur) {
+  auto phase2 = [&](int t, const char* v_cur, f32x16 (&s_nxt)[2]) __attribute__((always_inline)) {
     const int k0 = t * kTileN;
     if (k0 >= wlim_max) return;
     const int k1 = k0 + kTileN;
@@ -405,8 +416,6 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
           __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
         }
       }
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
     } else {
       pv(v_cur, pop);
     }
@@ -426,7 +435,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   // Each wave waits for its own loads and its own LDS reads, then a bare
   // barrier (a workgroup fence would drain every load in flight) makes the
   // tile whole and the stage about to be refilled unread.
-  auto wait_tile = [&]() {
+  auto wait_tile = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * LOADS, 0));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -439,9 +448,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
-  qk(sK0, s_cur);
-  if (kTileN > wlim_min) mask(0, s_cur);
-  mx_cur = rowmax(s_cur);
+  qk(sK0, sA);
+  if (kTileN > wlim_min) mask(0, sA);
+  mx_cur = rowmax(sA);
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
   __builtin_amdgcn_s_barrier();  // every wave is done with K(0)
   asm volatile("" ::: "memory");
@@ -451,17 +460,17 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   for (int t = 0; t < n_tiles; t += 2) {
     wait_tile();  // K(t+1) in sK1; sV1 (V(t-1)) read by every wave
     issue(t + 1, sV1, false);
-    phase1(t, sK1);
+    phase1(t, sK1, sA, sB);
     wait_tile();  // V(t) in sV0; sK1 (K(t+1)) read by every wave
     issue(t + 3, sK1, true);
-    phase2(t, sV0);
+    phase2(t, sV0, sB);
     if (t + 1 >= n_tiles) break;
     wait_tile();  // K(t+2) in sK0; sV0 (V(t)) read by every wave
     issue(t + 2, sV0, false);
-    phase1(t + 1, sK0);
+    phase1(t + 1, sK0, sB, sA);
     wait_tile();  // V(t+1) in sV1; sK0 (K(t+2)) read by every wave
     issue(t + 4, sK0, true);
-    phase2(t + 1, sV1);
+    phase2(t + 1, sV1, sA);
   }
   // Tiles past the last one were issued too: drain before the work-group's
   // LDS can be handed to another.
