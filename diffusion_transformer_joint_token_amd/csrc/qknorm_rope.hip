@@ -13,7 +13,9 @@
 // double precision before the final fp32 sincos, and shared by every head.
 // A group of LPH lanes owns one head; each lane holds a 16-byte chunk of it
 // (8 bf16 or 4 fp32), so loads and stores are full 16-byte vectors and a
-// head's sum of squares is a butterfly over LPH lanes.
+// head's sum of squares is a butterfly over LPH lanes.  When a head's chunk
+// count is not a power of two (head_dim 72 in bf16: 9 chunks) a flat mapping
+// of (head, chunk) items over 1-4 tokens per work-group is used instead.
 
 #include "device_common.h"
 #include "kernels.h"
@@ -160,10 +162,139 @@ __global__ __launch_bounds__(kThreads) void qknorm_rope_kernel(QkNormRopeArgs a)
   }
 }
 
+// Flat mapping for any number of 16-byte chunks per head (CPH = D / EPC):
+// the TPW tokens of a work-group hold TPW * (H + H_kv) * CPH (head, chunk)
+// items, dealt to the threads in order, so a head of 9 chunks (head_dim 72 in
+// bf16) does not leave 7 of 16 lanes idle.  A head's sum of squares is formed
+// through LDS: each item stores its partial, and after a barrier each item
+// adds the CPH partials of its head.
+constexpr int kFlatItems = 4;  // items per thread kept in flight
+constexpr int kFlatTokens = 4; // most tokens per work-group
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void qknorm_rope_flat_kernel(QkNormRopeArgs a, int tpw) {
+  constexpr int EPC = Elem<T>::kPerChunk;
+  __shared__ float2 s_cs[kFlatTokens][kMaxPairs];
+  __shared__ float s_ss[kThreads * kFlatItems];
+
+  const int tid = threadIdx.x;
+  const int b = blockIdx.y;
+  const int D = a.D;
+  const int cph = D / EPC;
+  const int nvh = a.H + a.Hk;
+  const int per_tok = nvh * cph;
+  const int s0 = blockIdx.x * tpw;
+  const int n_items = min(tpw, a.S - s0) * per_tok;
+
+  // Decode and load this thread's items: item = tt * per_tok + vh * cph + c.
+  int it_vh[kFlatItems], it_c[kFlatItems], it_t[kFlatItems];
+  u32x4 raw[kFlatItems];
+#pragma unroll
+  for (int k = 0; k < kFlatItems; ++k) {
+    const int item = tid + k * kThreads;
+    const int tt = item / per_tok;
+    const int rem = item - tt * per_tok;
+    const int vh = rem / cph;
+    it_t[k] = tt;
+    it_vh[k] = vh;
+    it_c[k] = rem - vh * cph;
+    raw[k] = u32x4{0, 0, 0, 0};
+    if (item < n_items) {
+      const int s = s0 + tt;
+      const T* src;
+      if (vh < a.H)
+        src = reinterpret_cast<const T*>(a.q) + b * a.qs[0] + (int64_t)s * a.qs[1] + vh * a.qs[2];
+      else
+        src = reinterpret_cast<const T*>(a.k) + b * a.ks[0] + (int64_t)s * a.ks[1] + (vh - a.H) * a.ks[2];
+      raw[k] = *reinterpret_cast<const u32x4*>(src + it_c[k] * EPC);
+    }
+  }
+  // Rotary phases of the work-group's tokens (as in the per-head kernel).
+  for (int p = tid; p < tpw * (D / 2); p += kThreads) {
+    const int tt = p / (D / 2), j = p - tt * (D / 2);
+    const int s = min(s0 + tt, a.S - 1);
+    const double phase = (double)a.pos[3 * s + a.pair_axis[j]] * a.omega[j];
+    const double turns = rint(phase * 0.15915494309189535);  // 1 / (2 pi)
+    const float red = (float)fma(-turns, 6.283185307179586, phase);
+    float sn, cs;
+    sincosf(red, &sn, &cs);
+    s_cs[tt][j] = make_float2(cs, sn);
+  }
+  // Partial sums of squares.
+  float x[kFlatItems][EPC];
+#pragma unroll
+  for (int k = 0; k < kFlatItems; ++k) {
+    Elem<T>::unpack(raw[k], x[k]);
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < EPC; ++i) ss = fmaf(x[k][i], x[k][i], ss);
+    s_ss[tid + k * kThreads] = ss;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kFlatItems; ++k) {
+    const int item = tid + k * kThreads;
+    if (item >= n_items) continue;
+    const int head0 = item - it_c[k];  // first item of this head
+    float ss = 0.f;
+    for (int c = 0; c < cph; ++c) ss += s_ss[head0 + c];
+    const bool is_q = it_vh[k] < a.H;
+    const float inv = 1.0f / sqrtf(ss / (float)D + a.eps) * (is_q ? a.q_scale : 1.0f);
+    float wv[EPC];
+    {
+      const T* wp = reinterpret_cast<const T*>(is_q ? a.wq : a.wk);
+      if (wp != nullptr) {
+        Elem<T>::unpack(*reinterpret_cast<const u32x4*>(wp + it_c[k] * EPC), wv);
+      } else {
+#pragma unroll
+        for (int i = 0; i < EPC; ++i) wv[i] = 1.0f;
+      }
+    }
+    float y[EPC];
+#pragma unroll
+    for (int i = 0; i < EPC; ++i) y[i] = x[k][i] * inv * wv[i];
+#pragma unroll
+    for (int i = 0; i < EPC / 2; ++i) {
+      const float2 cs = s_cs[it_t[k]][(it_c[k] * EPC) / 2 + i];
+      const float y0 = y[2 * i], y1 = y[2 * i + 1];
+      y[2 * i] = y0 * cs.x - y1 * cs.y;
+      y[2 * i + 1] = y0 * cs.y + y1 * cs.x;
+    }
+    const int s = s0 + it_t[k];
+    T* dst;
+    if (is_q)
+      dst = reinterpret_cast<T*>(a.qo) + b * a.qos[0] + (int64_t)s * a.qos[1] + it_vh[k] * a.qos[2];
+    else
+      dst = reinterpret_cast<T*>(a.ko) + b * a.kos[0] + (int64_t)s * a.kos[1] + (it_vh[k] - a.H) * a.kos[2];
+    *reinterpret_cast<u32x4*>(dst + it_c[k] * EPC) = Elem<T>::pack(y);
+  }
+}
+
 template <typename T>
 hipError_t launch_typed(const QkNormRopeArgs& a, hipStream_t stream) {
   constexpr int EPC = Elem<T>::kPerChunk;
   const int chunks = a.D / EPC;
+  const int per_tok = (a.H + a.Hk) * chunks;
+  // Tokens per work-group: the count (1, 2 or 4) that leaves the fewest idle
+  // item slots, within the items a work-group keeps in flight.
+  // A power-of-two chunk count fills whole lane groups: one head per group
+  // with a butterfly sum is faster there.
+  int tpw = 0;
+  long best = -1;
+  const bool pow2 = (chunks & (chunks - 1)) == 0;
+  for (int t = 1; !pow2 && t <= kFlatTokens; t *= 2) {
+    const long items = (long)t * per_tok;
+    if (items > (long)kThreads * kFlatItems) break;
+    const long slots = (items + kThreads - 1) / kThreads * kThreads;
+    const long waste = (slots - items) * 4 / t;  // idle slots per token
+    if (best < 0 || waste < best) { best = waste; tpw = t; }
+  }
+  if (tpw > 0) {
+    dim3 grid((a.S + tpw - 1) / tpw, a.B);
+    hipLaunchKernelGGL((qknorm_rope_flat_kernel<T>), grid, dim3(kThreads), 0, stream, a, tpw);
+    return hipGetLastError();
+  }
+  // One head per lane group, looping over the heads.
   int lph = 1;
   while (lph < chunks) lph <<= 1;
   dim3 grid(a.S, a.B);
