@@ -30,8 +30,8 @@
 //  * Softmax in the exp2 domain; the running max is only moved when a row's
 //    new maximum exceeds it by more than 8 (log2 units), so O is rarely
 //    rescaled and probabilities stay <= 2^8.
-//  * Work-groups are ordered heaviest query tile first and mapped so that all
-//    query tiles of one (batch, head) share an XCD (and its L2).
+//  * All query tiles of one (batch, head) run on one XCD (and its L2); the
+//    light low query tiles of each XCD go out last.
 
 #include <cmath>
 
@@ -51,11 +51,32 @@ constexpr int PF_V = 2;  // V^T operands read this many MFMAs ahead
 
 __device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 
-// Work-group index -> (batch*head, query tile), heaviest query tile first and
-// all tiles of one (batch, head) on one XCD (work-groups are dealt to the 8
-// XCDs round-robin).
+// Work-group index -> (batch*head, query tile).  Work-groups are dealt to the
+// 8 XCDs round-robin; each XCD gets whole (batch, head) units, so the query
+// tiles of one unit share that XCD's L2.  A query tile's work (its rows' key
+// bounds) never decreases along the sequence, so the lowest quarter of the
+// query tiles (the causal text rows of a block-causal sequence) are the light
+// ones: each XCD first runs its units one after another, last query tile
+// first, over the upper three quarters, then the lowest quarter across all
+// its units, last tile first, so light tiles fill the tail instead of
+// delaying heavy ones.
 __device__ __forceinline__ void map_block(int id, int nblocks, int n_qtiles, int& bh, int& qtile) {
   const int per = nblocks >> 3;
+  if (id < per * 8 && per % n_qtiles == 0) {
+    const int x = id & 7, j = id >> 3;  // XCD, position in its queue
+    const int units = per / n_qtiles;
+    const int low = n_qtiles >> 2;
+    const int hi = n_qtiles - low;
+    if (j < units * hi) {
+      bh = x * units + j / hi;
+      qtile = n_qtiles - 1 - j % hi;
+    } else {
+      const int k = j - units * hi;
+      bh = x * units + k % units;
+      qtile = low - 1 - k / units;
+    }
+    return;
+  }
   int logical = id;
   if (id < per * 8) logical = (id & 7) * per + (id >> 3);
   bh = logical / n_qtiles;
