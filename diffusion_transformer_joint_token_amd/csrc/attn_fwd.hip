@@ -53,27 +53,28 @@ __device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >>
 
 // Work-group index -> (batch*head, query tile).  Work-groups are dealt to the
 // 8 XCDs round-robin; each XCD gets whole (batch, head) units, so the query
-// tiles of one unit share that XCD's L2.  A query tile's work (its rows' key
-// bounds) never decreases along the sequence, so the lowest quarter of the
-// query tiles (the causal text rows of a block-causal sequence) are the light
-// ones: each XCD first runs its units one after another, last query tile
-// first, over the upper three quarters, then the lowest quarter across all
-// its units, last tile first, so light tiles fill the tail instead of
-// delaying heavy ones.
-__device__ __forceinline__ void map_block(int id, int nblocks, int n_qtiles, int& bh, int& qtile) {
+// tiles of one unit share that XCD's L2.  Under the block-causal mask a query
+// tile's work (its rows' key bounds) never decreases along the sequence, so
+// the lowest fifth of the query tiles (the causal text rows of a joint
+// sequence) are the light ones: each XCD first runs its units one after
+// another, last query tile first, over the upper tiles, then the low tiles
+// the same way, so light tiles fill the tail instead of delaying heavy ones
+// and each unit's keys are re-read at most once.  Under the full mask every
+// tile does the same work and the order is unit by unit.
+__device__ __forceinline__ void map_block(int id, int nblocks, int n_qtiles, bool causal, int& bh, int& qtile) {
   const int per = nblocks >> 3;
   if (id < per * 8 && per % n_qtiles == 0) {
     const int x = id & 7, j = id >> 3;  // XCD, position in its queue
     const int units = per / n_qtiles;
-    const int low = n_qtiles >> 2;
+    const int low = causal ? n_qtiles / 5 : 0;
     const int hi = n_qtiles - low;
     if (j < units * hi) {
       bh = x * units + j / hi;
       qtile = n_qtiles - 1 - j % hi;
     } else {
       const int k = j - units * hi;
-      bh = x * units + k % units;
-      qtile = low - 1 - k / units;
+      bh = x * units + k / low;
+      qtile = low - 1 - k % low;
     }
     return;
   }
@@ -137,7 +138,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   const int g = lane >> 5;  // k-group of the MFMA operands
   const int n_qtiles = (a.Snew + 32 * NW - 1) / (32 * NW);
   int bh, qtile;
-  map_block(blockIdx.x, gridDim.x, n_qtiles, bh, qtile);
+  map_block(blockIdx.x, gridDim.x, n_qtiles, a.kv_limit != nullptr, bh, qtile);
   const int h = bh % a.H;
   const int b = bh / a.H;
   const int kvh = h / (a.H / a.Hk);
