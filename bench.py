@@ -18,6 +18,7 @@ cores for a bounded sample of query rows of the same workload.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -149,6 +150,79 @@ def time_gpu(step: Step, steps: int, warmup: int):
             "attn_ms_median": float(np.median(attn_ms))}
 
 
+def time_norm_cold(step: Step, reps: int = 30, copies: int = 3):
+    """K2 alone, rotating `copies` separate input copies so that the Q/K read
+    by one launch were not touched by the launches just before it (config
+    3's Q+K, 168 MB, would otherwise partly stay in the 256 MB Infinity
+    Cache)."""
+    torch, dit, w = step.torch, step.dit, step.w
+    P = w.prefix_len
+    qs = [step.q] + [step.q.clone() for _ in range(copies - 1)]
+    ks = [step.k] + [step.k.clone() for _ in range(copies - 1)]
+    scale = dit.prescaled_q_factor(w.head_dim)
+
+    def launch(i):
+        dit.qknorm_rope(qs[i % copies], ks[i % copies], step.meta.pos_ids[P:], w.axes, w.eps, step.wq, step.wk,
+                        q_out=step.qp, k_out=step.kp, q_scale=scale)
+    for i in range(copies):
+        launch(i)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(ev):
+        a.record(step.stream)
+        launch(i)
+        b.record(step.stream)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in ev]
+    del qs, ks
+    return {"ms_mean": float(np.mean(ms)), "ms_median": float(np.median(ms)), "ms_min": float(np.min(ms))}
+
+
+def multistep(step: Step, n_steps: int, reps: int, warmup: int, full_ms: float):
+    """Step 1 runs the whole joint sequence; its norm kernel writes K' of every
+    token, so rows [0, P) of that buffer are the cache (P = every token before
+    the target block: text and condition images, which do not change with the
+    timestep).  Steps 2..N re-run only the target block: norm+rope of its
+    tokens and the cached-prefix attention against the step-1 cache.  Returns
+    the timings, the amortised speedup over N full steps and whether the
+    cached rows equal the full-step rows bit for bit."""
+    torch, dit, w = step.torch, step.dit, step.w
+    last = w.layout[-1]
+    if last[0] != "I":
+        raise SystemExit("--multistep needs a sequence that ends with the target image block")
+    P = w.seq_len - last[1] * last[2] * last[3]
+    if P == 0 or w.prefix_len:
+        raise SystemExit("--multistep needs a workload with tokens before the target block and no cache of its own")
+    q_new, k_new, v_new = step.q[:, P:], step.k[:, P:], step.v[:, P:]
+    k_cache, v_cache = step.kp[:, :P], step.v[:, :P]
+    qp_new = torch.empty_like(q_new, memory_format=torch.contiguous_format)
+    kp_new = torch.empty_like(k_new, memory_format=torch.contiguous_format)
+    o_new = torch.empty_like(q_new, memory_format=torch.contiguous_format)
+    scale = dit.prescaled_q_factor(w.head_dim)
+
+    def cached():
+        dit.qknorm_rope(q_new, k_new, step.meta.pos_ids[P:], w.axes, w.eps, step.wq, step.wk,
+                        q_out=qp_new, k_out=kp_new, q_scale=scale)
+        dit.forward_cached(qp_new, k_cache, v_cache, kp_new, v_new, w.mask_mode, step.meta,
+                           softmax_scale=dit.LN2, out=o_new)
+    step.run()
+    for _ in range(warmup):
+        cached()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(o_new, step.o[:, P:]))
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record(step.stream)
+        cached()
+        b.record(step.stream)
+    torch.cuda.synchronize()
+    cached_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    amort = (full_ms + (n_steps - 1) * cached_ms) / n_steps
+    return {"steps": n_steps, "prefix_tokens": P, "target_tokens": w.seq_len - P, "full_step_ms": full_ms,
+            "cached_step_ms": cached_ms, "amortised_ms_per_step": amort, "speedup_vs_full_steps": full_ms / amort,
+            "cached_rows_equal_full_rows": same}
+
+
 def cpu_baseline(w: wl.Workload, drawn: wl.Drawn, budget_s: float = 12.0):
     """The fp64 oracle (as it stands) on the host: norm + rope of the sampled
     query rows, then their attention rows; rows drawn at random from the
@@ -251,6 +325,11 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=list(wl.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the host oracle timing")
+    ap.add_argument("--multistep", type=int, default=0, metavar="N",
+                    help="also time N denoising steps: one full step, then N-1 steps that recompute only the "
+                         "target block against the cached prefix K/V; adds a 'multistep' object to the line")
+    ap.add_argument("--shard-heads", type=int, default=1, metavar="K",
+                    help="run one GPU's share of a K-way head-sharded job: heads and kv_heads divided by K")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (the reference "
@@ -281,6 +360,13 @@ def main(argv=None) -> int:
         return 0
 
     w = wl.WORKLOADS[args.workload]
+    if args.shard_heads > 1:
+        K = args.shard_heads
+        if w.heads % K or w.kv_heads % K:
+            print("--shard-heads %d does not divide %d/%d heads" % (K, w.heads, w.kv_heads), file=sys.stderr)
+            return 2
+        w = dataclasses.replace(w, name="%s_heads_div%d" % (w.name, K), heads=w.heads // K,
+                                kv_heads=w.kv_heads // K)
     log("workload %s: B=%d H=%d/%d D=%d S=%d (queries %d) mask=%s dtype=%s" % (
         w.name, w.batch, w.heads, w.kv_heads, w.head_dim, w.seq_len, w.n_new, w.mask_mode, w.dtype))
     step = Step(w, "cuda")
@@ -294,6 +380,9 @@ def main(argv=None) -> int:
 
     t = time_gpu(step, args.steps, args.warmup)
     log("timing: %s" % json.dumps(t))
+    cold = time_norm_cold(step)
+    log("norm/rope with rotated inputs: %s" % json.dumps(cold))
+    props = torch.cuda.get_device_properties(0)
     value = flops / (t["step_ms"] * 1e-3) / 1e12
     attn_tflops = flops / (t["attn_ms_mean"] * 1e-3) / 1e12
     elem = 2 if w.dtype == "bf16" else 4
@@ -312,14 +401,24 @@ def main(argv=None) -> int:
                    "rope_axes": list(w.axes), "step": "token metadata + qk-rmsnorm/rope + attention"},
         "pct_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
         "attention_only": {"tflops": attn_tflops, "pct_bf16_peak": 100.0 * attn_tflops / PEAK_BF16_TFLOPS,
-                           "ms_mean": t["attn_ms_mean"], "ms_min": t["attn_ms_min"]},
+                           "ms_mean": t["attn_ms_mean"], "ms_median": t["attn_ms_median"],
+                           "ms_min": t["attn_ms_min"]},
         "qknorm_rope": {"ms": t["norm_ms"], "gbs": norm_bytes / (t["norm_ms"] * 1e-3) / 1e9,
                         "frac_hbm": norm_bytes / (t["norm_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                        "bytes": norm_bytes},
+                        "bytes": norm_bytes,
+                        "rotated_inputs": {"copies": 3, "ms_mean": cold["ms_mean"], "ms_median": cold["ms_median"],
+                                           "gbs": norm_bytes / (cold["ms_mean"] * 1e-3) / 1e9,
+                                           "frac_hbm": norm_bytes / (cold["ms_mean"] * 1e-3) / 1e9 / PEAK_HBM_GBS}},
+        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                   "compute_units": props.multi_processor_count},
         "token_metadata_ms": t["meta_ms"],
         "roofline": roofline,
         "cpu_baseline": None,
     }
+    if args.multistep:
+        ms = multistep(step, args.multistep, args.steps, args.warmup, t["step_ms"])
+        log("multistep: %s" % json.dumps(ms))
+        line["multistep"] = ms
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on host cores, ~%.0f s" % args.cpu_budget)
         cb = cpu_baseline(w, step.drawn, args.cpu_budget)
