@@ -27,6 +27,10 @@ float64 NumPy, slow and plain:
   independent implementation of the mask that the page says gives the same
   result.
 * ``attention.attention_bruteforce`` -- quadruple Python loops, tiny inputs.
+* ``key_padding.joint_key_valid`` -- the per-sample text mask
+  (``encoder_hidden_states_mask``) laid over the joint sequence as per-key
+  validity, which ``attention`` and ``attention_bruteforce`` take as
+  ``key_valid`` (QwenImage21Transformer2DModel API page, ``forward``).
 
 Pins: every function is pinned by tests under ``tests/`` that do not re-type
 its formula: closed forms, invariants (rotation preserves norms, relative
@@ -37,4 +41,4 @@ inputs, and hand-derived token-metadata fixtures under ``tests/golden``.
 The pages print no numeric worked example for this step, so no pin is a
 printed value; none of the functions is left unpinned.
 """
-from . import metadata, qknorm_rope, attention, pipeline  # noqa: F401
+from . import metadata, qknorm_rope, attention, pipeline, key_padding  # noqa: F401

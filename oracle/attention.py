@@ -16,10 +16,17 @@ Sources:
     repeating each KV head for its group of query heads (repeat_interleave), so
     query head h reads KV head h // (H / H_kv).
 
+  * same page, forward(encoder_hidden_states_mask): a per-sample boolean over
+    the text tokens marks the valid ones; padded text positions are excluded
+    from attention, i.e. as keys (``key_valid``, one flag per batch sample and
+    logical key position).
+
 Readings: the softmax scale is 1/sqrt(head_dim); "same image block" needs an
 image id >= 0 on both sides (text ids are -1 and never match); in the full
 mode every key is allowed.  lse is the natural-log log-sum-exp of the scaled
-logits over the allowed keys.
+logits over the allowed keys.  Padding removes keys only (a padded text
+position still has a query row, computed like any other); a row left with
+no allowed key has output 0 and lse -inf.
 """
 from __future__ import annotations
 
@@ -49,12 +56,13 @@ def allowed_matrix(q_index: np.ndarray, k_index: np.ndarray, image_ids: np.ndarr
 
 def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, image_ids: np.ndarray, mask_mode: str,
               scale: Optional[float] = None, q_offset: int = 0, rows: Optional[Sequence[int]] = None,
-              chunk: int = 2048) -> Tuple[np.ndarray, np.ndarray]:
+              chunk: int = 2048, key_valid: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
     """O = softmax(scale * Q K^T + M) V per (batch, head), GQA by head groups.
 
     q: [B, Sq, H, D]; k, v: [B, Sk, Hk, D] (keys cover the logical positions
     0..Sk-1).  Query row i sits at logical position q_offset + i (q_offset is
     the cached-prefix length).  rows: which query rows to compute (default all).
+    key_valid: optional bool [B, Sk]; False keys are excluded for that sample.
     Returns (o [B, len(rows), H, D], lse [B, H, len(rows)]).
     """
     q = np.asarray(q, dtype=np.float64)
@@ -73,17 +81,20 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, image_ids: np.ndarray
     k_index = np.arange(Sk)
     for c0 in range(0, rows.size, chunk):
         r = rows[c0:c0 + chunk]
-        allow = allowed_matrix(r + q_offset, k_index, image_ids, mask_mode)
+        allow_all = allowed_matrix(r + q_offset, k_index, image_ids, mask_mode)
         for b in range(B):
+            allow = allow_all if key_valid is None else allow_all & np.asarray(key_valid[b], dtype=bool)[None, :]
+            live = allow.any(axis=1)  # rows with at least one allowed key
             for h in range(H):
                 g = h // group
                 logits = scale * (q[b, r, h, :] @ k[b, :, g, :].T)
                 logits = np.where(allow, logits, -np.inf)
-                m = logits.max(axis=1, keepdims=True)
+                m = np.where(live, logits.max(axis=1), 0.0)[:, None]
                 p = np.exp(logits - m)
                 denom = p.sum(axis=1, keepdims=True)
-                out[b, c0:c0 + r.size, h, :] = (p @ v[b, :, g, :]) / denom
-                lse[b, h, c0:c0 + r.size] = (m + np.log(denom))[:, 0]
+                safe = np.where(live[:, None], denom, 1.0)
+                out[b, c0:c0 + r.size, h, :] = np.where(live[:, None], (p @ v[b, :, g, :]) / safe, 0.0)
+                lse[b, h, c0:c0 + r.size] = np.where(live, (m + np.log(safe))[:, 0], -np.inf)
     return out, lse
 
 
@@ -134,7 +145,7 @@ def attention_multipass(q: np.ndarray, k: np.ndarray, v: np.ndarray, image_ids: 
 
 
 def attention_bruteforce(q, k, v, image_ids, mask_mode: str, scale: Optional[float] = None,
-                         q_offset: int = 0):
+                         q_offset: int = 0, key_valid=None):
     """Quadruple Python loops with math.exp; tiny inputs only.  Returns nested
     lists o[b][i][h][d] and lse[b][h][i]."""
     B, Sq, H, D = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
@@ -156,11 +167,16 @@ def attention_bruteforce(q, k, v, image_ids, mask_mode: str, scale: Optional[flo
                     else:
                         same = image_ids[qi] >= 0 and image_ids[qi] == image_ids[j]
                         ok = j <= qi or same
+                    if key_valid is not None and not key_valid[b][j]:
+                        ok = False
                     if ok:
                         dot = 0.0
                         for d in range(D):
                             dot += float(q[b][i][h][d]) * float(k[b][j][g][d])
                         logits.append((j, scale * dot))
+                if not logits:  # every allowed key is padding
+                    lse[b][h][i] = -math.inf
+                    continue
                 m = max(val for _, val in logits)
                 weights = [(j, math.exp(val - m)) for j, val in logits]
                 total = sum(wt for _, wt in weights)

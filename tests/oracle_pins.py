@@ -15,6 +15,7 @@ import numpy as np
 import torch
 
 import oracle.attention as att
+import oracle.key_padding as kp
 import oracle.metadata as meta
 import oracle.qknorm_rope as qr
 from tests import goldens
@@ -323,8 +324,93 @@ def pin_lse_definition():
     assert np.allclose(o[0, :, 0, :], probs, rtol=1e-12, atol=1e-14)
 
 
+# --------------------------------------------------------------------------- key padding
+def pin_key_padding_fixtures():
+    """Hand-derived: the j-th text token of the joint sequence takes the j-th
+    flag of the per-sample text mask, image tokens are always valid
+    (QwenImage21Transformer2DModel API page, forward's
+    encoder_hidden_states_mask); a mask of the wrong length is a data error."""
+    # sequence: text, text, image, image, text, image
+    got = kp.joint_key_valid([0, 0, 1, 1, 0, 1], [[1, 0, 1], [0, 1, 1]])
+    assert got.tolist() == [[True, False, True, True, True, True],
+                            [False, True, True, True, True, True]]
+    # text after the images (condition-image layouts put text between blocks)
+    got = kp.joint_key_valid([1, 1, 0, 0], [[0, 1]])
+    assert got.tolist() == [[True, True, False, True]]
+    try:
+        kp.joint_key_valid([0, 1, 0], [[1, 1, 1]])
+    except kp.KeyPaddingError:
+        pass
+    else:
+        raise AssertionError("a text mask of the wrong length must be rejected")
+
+
+def _sdpa_masked(q, k, v, allowed):
+    """torch SDPA, float64, CPU, boolean attn_mask (True = attend); BSHD."""
+    tq, tk, tv = (torch.from_numpy(np.ascontiguousarray(x.transpose(0, 2, 1, 3))) for x in (q, k, v))
+    o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=torch.from_numpy(allowed))
+    return o.numpy().transpose(0, 2, 1, 3)
+
+
+def pin_key_padding_is_masked_sdpa():
+    """Block-causal attention with per-sample padded text keys equals torch SDPA
+    given the literal predicate AND the key flags; with every key valid it
+    equals attention without padding."""
+    mask, shapes = _layout_inputs((("T", 9), ("I", 1, 2, 4), ("T", 4), ("I", 1, 2, 2)))
+    ids = meta.build_token_metadata(mask, shapes)["image_ids"]
+    S = len(mask)
+    rng = np.random.default_rng(21)
+    q, k, v = (rng.standard_normal((2, S, 2, 8)) for _ in range(3))
+    n_text = int((np.asarray(mask) == 0).sum())
+    tv = rng.random((2, n_text)) < 0.6
+    tv[:, 0] = True  # keep one valid key for every row (rows without any are pinned below)
+    valid = kp.joint_key_valid(mask, tv)
+    o, _ = att.attention(q, k, v, ids, "block_causal", key_valid=valid)
+    pred = np.array([[j <= i or (ids[i] >= 0 and ids[i] == ids[j]) for j in range(S)] for i in range(S)])
+    for b in range(2):
+        ref = _sdpa_masked(q[b:b + 1], k[b:b + 1], v[b:b + 1], pred & valid[b][None, :])
+        assert np.allclose(o[b:b + 1], ref, rtol=1e-10, atol=1e-12), b
+    o_all, lse_all = att.attention(q, k, v, ids, "block_causal", key_valid=np.ones((2, S), bool))
+    o_ref, lse_ref = att.attention(q, k, v, ids, "block_causal")
+    assert np.array_equal(o_all, o_ref) and np.array_equal(lse_all, lse_ref)
+
+
+def pin_key_padding_is_compaction():
+    """Under the full mask, padded keys behave as if they were removed: equal to
+    torch SDPA over K and V with those rows deleted."""
+    rng = np.random.default_rng(22)
+    S = 20
+    q, k, v = (rng.standard_normal((1, S, 3, 16)) for _ in range(3))
+    valid = np.ones((1, S), bool)
+    valid[0, [2, 3, 11, 19]] = False
+    o, _ = att.attention(q, k, v, np.zeros(S, int), "full", key_valid=valid)
+    keep = valid[0]
+    ref = _sdpa(q, k[:, keep], v[:, keep])
+    assert np.allclose(o, ref, rtol=1e-10, atol=1e-12)
+
+
+def pin_key_padding_bruteforce_and_empty_rows():
+    """Vectorised == loops with padding; a row whose allowed keys are all padded
+    (leading padded text under the block-causal rule) has output 0 and lse -inf."""
+    mask, shapes = _layout_inputs((("T", 4), ("I", 1, 2, 2)))
+    ids = meta.build_token_metadata(mask, shapes)["image_ids"]
+    S = len(mask)
+    rng = np.random.default_rng(23)
+    q, k, v = (rng.standard_normal((2, S, 2, 4)) for _ in range(3))
+    valid = kp.joint_key_valid(mask, [[0, 0, 1, 1], [1, 0, 0, 1]])
+    o, lse = att.attention(q, k, v, ids, "block_causal", key_valid=valid)
+    ob, lb = att.attention_bruteforce(_nested(q), _nested(k), _nested(v), list(ids), "block_causal",
+                                      key_valid=valid.tolist())
+    assert np.allclose(o, np.asarray(ob), rtol=1e-11, atol=1e-13)
+    assert np.allclose(lse, np.asarray(lb), rtol=1e-11, atol=1e-13)
+    # sample 0: rows 0 and 1 see only keys 0..1, both padded
+    assert np.all(o[0, :2] == 0.0) and np.all(np.isneginf(lse[0, :, :2]))
+    assert np.all(np.isfinite(lse[0, :, 2:])) and np.all(np.isfinite(lse[1]))
+
+
 ALL_PINS = [pin_metadata_goldens, pin_kv_limit_is_predicate_prefix, pin_metadata_errors,
             pin_rmsnorm_closed_forms, pin_rope_rotation, pin_rope_pairing_and_ladder, pin_rope_relative,
             pin_full_is_sdpa, pin_text_only_is_causal, pin_gqa_is_repeat_interleave,
             pin_singlepass_equals_multipass, pin_adjacent_blocks_stay_separate, pin_cached_equals_full,
-            pin_bruteforce_tiny, pin_lse_definition]
+            pin_bruteforce_tiny, pin_lse_definition, pin_key_padding_fixtures, pin_key_padding_is_masked_sdpa,
+            pin_key_padding_is_compaction, pin_key_padding_bruteforce_and_empty_rows]

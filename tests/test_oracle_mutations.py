@@ -4,6 +4,7 @@ import numpy as np
 import pytest
 
 import oracle.attention as att
+import oracle.key_padding as kp
 import oracle.metadata as meta
 import oracle.qknorm_rope as qr
 from tests import oracle_pins as pins
@@ -85,17 +86,44 @@ qr_rope_orig = qr.rope
 att_attention_orig = att.attention
 
 
-def _attention_gqa_modulo(q, k, v, image_ids, mask_mode, scale=None, q_offset=0, rows=None, chunk=2048):
+def _attention_gqa_modulo(q, k, v, image_ids, mask_mode, scale=None, q_offset=0, rows=None, chunk=2048,
+                          key_valid=None):
     # Mistake: query head h reads KV head h % H_kv instead of h // G.
     H, Hk = q.shape[2], k.shape[2]
     perm = [h % Hk for h in range(H)]
     ke = np.asarray(k)[:, :, perm]
     ve = np.asarray(v)[:, :, perm]
-    return att_attention_orig(q, ke, ve, image_ids, mask_mode, scale, q_offset, rows, chunk)
+    return att_attention_orig(q, ke, ve, image_ids, mask_mode, scale, q_offset, rows, chunk, key_valid)
 
 
-def _attention_no_scale(q, k, v, image_ids, mask_mode, scale=None, q_offset=0, rows=None, chunk=2048):
-    return att_attention_orig(q, k, v, image_ids, mask_mode, 1.0, q_offset, rows, chunk)
+def _attention_no_scale(q, k, v, image_ids, mask_mode, scale=None, q_offset=0, rows=None, chunk=2048,
+                        key_valid=None):
+    return att_attention_orig(q, k, v, image_ids, mask_mode, 1.0, q_offset, rows, chunk, key_valid)
+
+
+def _attention_padding_masks_queries(q, k, v, image_ids, mask_mode, scale=None, q_offset=0, rows=None,
+                                     chunk=2048, key_valid=None):
+    # Mistake: padding removes the padded positions' query rows instead of their keys.
+    o, lse = att_attention_orig(q, k, v, image_ids, mask_mode, scale, q_offset, rows, chunk)
+    if key_valid is not None:
+        r = np.arange(np.asarray(q).shape[1]) if rows is None else np.asarray(rows)
+        dead = ~np.asarray(key_valid, bool)[:, r + q_offset]
+        o = np.where(dead[:, :, None, None], 0.0, o)
+    return o, lse
+
+
+kp_orig = kp.joint_key_valid
+
+
+def _key_valid_by_position(image_pad_mask, text_valid):
+    # Mistake: the text flag is indexed by sequence position instead of text ordinal.
+    mask = np.asarray(image_pad_mask).reshape(-1)
+    tv = np.asarray(text_valid, bool)
+    out = np.ones((tv.shape[0], mask.size), bool)
+    for s in range(mask.size):
+        if mask[s] == 0:
+            out[:, s] = tv[:, min(s, tv.shape[1] - 1)]
+    return out
 
 
 def _metadata_merge_runs(image_pad_mask, img_shapes, pos_mode="centered_fhw"):
@@ -160,6 +188,8 @@ MUTATIONS = [
     ("metadata_merges_adjacent_images", meta, "build_token_metadata", _metadata_merge_runs),
     ("metadata_kv_limit_off_by_one", meta, "build_token_metadata", _metadata_kv_limit_off_by_one),
     ("metadata_positions_uncentred", meta, "build_token_metadata", _metadata_uncentred),
+    ("padding_masks_queries_not_keys", att, "attention", _attention_padding_masks_queries),
+    ("padding_flag_by_position", kp, "joint_key_valid", _key_valid_by_position),
 ]
 
 
