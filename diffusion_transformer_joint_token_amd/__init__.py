@@ -1,11 +1,14 @@
 """Joint text+image DiT attention step for MI355X (gfx950).
 
-Four entry points, each a thin binding of the C ABI in include/dit_attn.h:
-``build_token_metadata`` -> ``qknorm_rope`` -> ``forward`` / ``forward_cached``.
-Importing the package loads the in-tree ``libdit_attn.so`` and fails if it is
-missing; there is no other implementation behind these names.
+Thin bindings of the C ABI in include/dit_attn.h:
+``build_token_metadata`` -> ``qknorm_rope`` -> ``forward`` / ``forward_cached``,
+with ``build_key_valid`` and the ``key_valid`` argument of the two attention
+calls for padded text tokens.  Importing the package loads the in-tree
+``libdit_attn.so`` and fails if it is missing; there is no other
+implementation behind these names.
 """
-from .api import (LN2, LOG2E, DitAttnError, TokenMeta, build_token_metadata,  # noqa: F401
-                  dit_attn_build_token_metadata, dit_attn_forward, dit_attn_forward_cached, dit_attn_qknorm_rope,
-                  forward, forward_cached, prescaled_q_factor, qknorm_rope)
+from .api import (LN2, LOG2E, DitAttnError, KeyValid, TokenMeta, build_key_valid,  # noqa: F401
+                  build_token_metadata, dit_attn_build_key_valid, dit_attn_build_token_metadata, dit_attn_forward,
+                  dit_attn_forward_cached, dit_attn_forward_cached_padded, dit_attn_forward_padded,
+                  dit_attn_qknorm_rope, forward, forward_cached, prescaled_q_factor, qknorm_rope)
 from ._lib import LIB_PATH  # noqa: F401

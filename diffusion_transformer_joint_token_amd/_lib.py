@@ -18,8 +18,9 @@ MASK_FULL, MASK_BLOCK_CAUSAL = 0, 1
 POS_CENTERED_FHW, POS_GRID_HW = 0, 1
 MAX_IMAGES = 64
 
-EXPORTED = ("dit_attn_build_token_metadata", "dit_attn_qknorm_rope", "dit_attn_forward",
-            "dit_attn_forward_cached", "dit_attn_status_string")
+EXPORTED = ("dit_attn_build_token_metadata", "dit_attn_build_key_valid", "dit_attn_qknorm_rope",
+            "dit_attn_forward", "dit_attn_forward_cached", "dit_attn_forward_padded",
+            "dit_attn_forward_cached_padded", "dit_attn_status_string")
 
 
 class TokenMetaStruct(ctypes.Structure):
@@ -28,7 +29,7 @@ class TokenMetaStruct(ctypes.Structure):
 
 
 Strides3 = ctypes.c_int64 * 3
-i32, vp, f32 = ctypes.c_int32, ctypes.c_void_p, ctypes.c_float
+i32, i64, vp, f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float
 
 
 def _load() -> ctypes.CDLL:
@@ -38,6 +39,7 @@ def _load() -> ctypes.CDLL:
     lib = ctypes.CDLL(LIB_PATH)
     lib.dit_attn_build_token_metadata.argtypes = [vp, i32, ctypes.POINTER(i32), i32, i32,
                                                   ctypes.POINTER(TokenMetaStruct), vp, vp]
+    lib.dit_attn_build_key_valid.argtypes = [vp, i32, vp, i32, i32, i64, vp, i64, vp, vp]
     lib.dit_attn_qknorm_rope.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                          Strides3, Strides3, Strides3, Strides3, vp, i32,
                                          ctypes.POINTER(i32), f32, f32, f32, i32, vp]
@@ -45,6 +47,11 @@ def _load() -> ctypes.CDLL:
                                      ctypes.POINTER(TokenMetaStruct), f32, i32, vp]
     lib.dit_attn_forward_cached.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                             Strides3 * 6, i32, ctypes.POINTER(TokenMetaStruct), f32, i32, vp]
+    lib.dit_attn_forward_padded.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, Strides3 * 4, i32,
+                                            ctypes.POINTER(TokenMetaStruct), vp, i64, f32, i32, vp]
+    lib.dit_attn_forward_cached_padded.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                                   Strides3 * 6, i32, ctypes.POINTER(TokenMetaStruct), vp, i64,
+                                                   f32, i32, vp]
     for name in EXPORTED[:-1]:
         getattr(lib, name).restype = ctypes.c_int
     lib.dit_attn_status_string.argtypes = [i32]

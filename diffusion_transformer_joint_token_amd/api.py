@@ -1,4 +1,4 @@
-"""Python binding of the C ABI: the same four entry points on torch tensors.
+"""Python binding of the C ABI: the same entry points on torch tensors.
 
 Argument marshalling only: every step of the computation runs in the gfx950
 kernels of libdit_attn.so.  torch provides device memory and the current HIP
@@ -16,9 +16,10 @@ import torch
 from . import _lib
 from ._lib import DitAttnError, check, lib
 
-__all__ = ["TokenMeta", "DitAttnError", "LN2", "LOG2E", "prescaled_q_factor", "dit_attn_build_token_metadata", "dit_attn_qknorm_rope",
-           "dit_attn_forward", "dit_attn_forward_cached", "build_token_metadata", "qknorm_rope", "forward",
-           "forward_cached"]
+__all__ = ["TokenMeta", "KeyValid", "DitAttnError", "LN2", "LOG2E", "prescaled_q_factor",
+           "dit_attn_build_token_metadata", "dit_attn_build_key_valid", "dit_attn_qknorm_rope", "dit_attn_forward",
+           "dit_attn_forward_cached", "dit_attn_forward_padded", "dit_attn_forward_cached_padded",
+           "build_token_metadata", "build_key_valid", "qknorm_rope", "forward", "forward_cached"]
 
 _POS = {"centered_fhw": _lib.POS_CENTERED_FHW, "grid_hw": _lib.POS_GRID_HW}
 
@@ -112,6 +113,49 @@ def dit_attn_build_token_metadata(image_pad_mask: torch.Tensor, img_shapes: Sequ
     return meta
 
 
+@dataclass
+class KeyValid:
+    """Per-sample key validity bits (bit j of word t of row b: key 64 t + j of
+    sample b may be attended), stored as int64 words, and the builder's status."""
+    bits: torch.Tensor    # int64 [B, words]
+    status: torch.Tensor  # int32 [1]
+
+    def check(self) -> None:
+        """Synchronise with the producing stream and raise on a data error."""
+        check(int(self.status.item()), "dit_attn_build_key_valid (device status)")
+
+
+def dit_attn_build_key_valid(image_pad_mask: torch.Tensor, text_valid: torch.Tensor,
+                             out: Optional[KeyValid] = None, stream=None) -> KeyValid:
+    """Key validity of the joint sequence from the text mask (text_valid:
+    bool/uint8 [B, n_text], n_text = number of text tokens in the layout)."""
+    mask = image_pad_mask.view(torch.uint8) if image_pad_mask.dtype == torch.bool else image_pad_mask
+    if mask.dtype != torch.uint8 or mask.dim() != 1 or not mask.is_contiguous():
+        raise DitAttnError(_lib.ERR_SHAPE, "image_pad_mask must be a contiguous 1-D uint8/bool tensor")
+    tv = text_valid.view(torch.uint8) if text_valid.dtype == torch.bool else text_valid
+    if tv.dtype != torch.uint8 or tv.dim() != 2 or (tv.shape[1] > 1 and tv.stride(1) != 1):
+        raise DitAttnError(_lib.ERR_SHAPE, "text_valid must be [B, n_text] uint8/bool with unit inner stride")
+    S = mask.numel()
+    B, n_text = tv.shape
+    words = (S + 63) // 64
+    kv = out if out is not None else KeyValid(torch.empty(B, max(1, words), dtype=torch.int64, device=mask.device),
+                                              torch.empty(1, dtype=torch.int32, device=mask.device))
+    if kv.bits.dtype != torch.int64 or kv.bits.dim() != 2 or kv.bits.shape[0] != B or kv.bits.stride(1) != 1:
+        raise DitAttnError(_lib.ERR_SHAPE, "key_valid bits must be int64 [B, words] with unit inner stride")
+    st = lib.dit_attn_build_key_valid(mask.data_ptr(), S, tv.data_ptr() if n_text else None, B, n_text,
+                                      tv.stride(0) if B > 1 else n_text, kv.bits.data_ptr(), kv.bits.stride(0)
+                                      if B > 1 else kv.bits.shape[1], kv.status.data_ptr(), _stream(stream))
+    check(st, "dit_attn_build_key_valid")
+    return kv
+
+
+def _key_bits(key_valid) -> Tuple[int, int]:
+    bits = key_valid.bits if isinstance(key_valid, KeyValid) else key_valid
+    if bits.dtype != torch.int64 or bits.dim() != 2 or bits.stride(1) != 1:
+        raise DitAttnError(_lib.ERR_SHAPE, "key_valid bits must be int64 [B, words] with unit inner stride")
+    return bits.data_ptr(), bits.stride(0) if bits.shape[0] > 1 else bits.shape[1]
+
+
 def dit_attn_qknorm_rope(q: torch.Tensor, k: torch.Tensor, pos_ids: torch.Tensor, axes_dims: Sequence[int],
                          eps: float, q_weight: Optional[torch.Tensor] = None,
                          k_weight: Optional[torch.Tensor] = None, rope_theta: float = 10000.0,
@@ -152,7 +196,10 @@ def _lse_buffer(return_lse: bool, B: int, H: int, S: int, device) -> Optional[to
 
 def dit_attn_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask_mode: Union[str, int] = "full",
                      meta: Optional[TokenMeta] = None, softmax_scale: Optional[float] = None,
-                     out: Optional[torch.Tensor] = None, return_lse: bool = False, stream=None):
+                     out: Optional[torch.Tensor] = None, return_lse: bool = False, stream=None,
+                     key_valid=None):
+    """Attention over the joint sequence; with key_valid (a KeyValid or its
+    int64 bits [B, words]) padded keys are left out (dit_attn_forward_padded)."""
     B, S, H, D = q.shape
     Hk = k.shape[2]
     if k.shape != (B, S, Hk, D) or v.shape != (B, S, Hk, D):
@@ -167,17 +214,27 @@ def dit_attn_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask_mod
     mode = _MASK[mask_mode] if isinstance(mask_mode, str) else int(mask_mode)
     ms = meta.struct() if meta is not None else None
     scale = 0.0 if softmax_scale is None else float(softmax_scale)
-    st = lib.dit_attn_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _ptr(lse), B, S, H, Hk, D,
-                              strides, mode, ctypes.byref(ms) if ms is not None else None, scale, dt,
-                              _stream(stream))
-    check(st, "dit_attn_forward")
+    msp = ctypes.byref(ms) if ms is not None else None
+    if key_valid is None:
+        st = lib.dit_attn_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _ptr(lse), B, S, H, Hk, D,
+                                  strides, mode, msp, scale, dt, _stream(stream))
+        check(st, "dit_attn_forward")
+    else:
+        kb, kbs = _key_bits(key_valid)
+        st = lib.dit_attn_forward_padded(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _ptr(lse), B, S, H,
+                                         Hk, D, strides, mode, msp, kb, kbs, scale, dt, _stream(stream))
+        check(st, "dit_attn_forward_padded")
     return (o, lse) if return_lse else o
 
 
 def dit_attn_forward_cached(q_new: torch.Tensor, k_cache: Optional[torch.Tensor], v_cache: Optional[torch.Tensor],
                             k_new: torch.Tensor, v_new: torch.Tensor, mask_mode: Union[str, int] = "block_causal",
                             meta: Optional[TokenMeta] = None, softmax_scale: Optional[float] = None,
-                            out: Optional[torch.Tensor] = None, return_lse: bool = False, stream=None):
+                            out: Optional[torch.Tensor] = None, return_lse: bool = False, stream=None,
+                            key_valid=None):
+    """Attention of the new tokens against cache + new keys; with key_valid
+    (bits over the logical sequence) padded keys are left out
+    (dit_attn_forward_cached_padded)."""
     B, S_new, H, D = q_new.shape
     Hk = k_new.shape[2]
     P = 0 if k_cache is None else k_cache.shape[1]
@@ -197,15 +254,35 @@ def dit_attn_forward_cached(q_new: torch.Tensor, k_cache: Optional[torch.Tensor]
     mode = _MASK[mask_mode] if isinstance(mask_mode, str) else int(mask_mode)
     ms = meta.struct() if meta is not None else None
     scale = 0.0 if softmax_scale is None else float(softmax_scale)
-    st = lib.dit_attn_forward_cached(q_new.data_ptr(), _ptr(k_cache) if P > 0 else None,
-                                     _ptr(v_cache) if P > 0 else None, k_new.data_ptr(), v_new.data_ptr(),
-                                     o.data_ptr(), _ptr(lse), B, P, S_new, H, Hk, D, strides, mode,
-                                     ctypes.byref(ms) if ms is not None else None, scale, dt, _stream(stream))
-    check(st, "dit_attn_forward_cached")
+    msp = ctypes.byref(ms) if ms is not None else None
+    kc, vc = (_ptr(k_cache), _ptr(v_cache)) if P > 0 else (None, None)
+    if key_valid is None:
+        st = lib.dit_attn_forward_cached(q_new.data_ptr(), kc, vc, k_new.data_ptr(), v_new.data_ptr(), o.data_ptr(),
+                                         _ptr(lse), B, P, S_new, H, Hk, D, strides, mode, msp, scale, dt,
+                                         _stream(stream))
+        check(st, "dit_attn_forward_cached")
+    else:
+        kb, kbs = _key_bits(key_valid)
+        st = lib.dit_attn_forward_cached_padded(q_new.data_ptr(), kc, vc, k_new.data_ptr(), v_new.data_ptr(),
+                                                o.data_ptr(), _ptr(lse), B, P, S_new, H, Hk, D, strides, mode, msp,
+                                                kb, kbs, scale, dt, _stream(stream))
+        check(st, "dit_attn_forward_cached_padded")
     return (o, lse) if return_lse else o
 
 
+def dit_attn_forward_padded(q, k, v, key_valid, mask_mode="full", meta=None, softmax_scale=None, out=None,
+                            return_lse=False, stream=None):
+    return dit_attn_forward(q, k, v, mask_mode, meta, softmax_scale, out, return_lse, stream, key_valid=key_valid)
+
+
+def dit_attn_forward_cached_padded(q_new, k_cache, v_cache, k_new, v_new, key_valid, mask_mode="block_causal",
+                                   meta=None, softmax_scale=None, out=None, return_lse=False, stream=None):
+    return dit_attn_forward_cached(q_new, k_cache, v_cache, k_new, v_new, mask_mode, meta, softmax_scale, out,
+                                   return_lse, stream, key_valid=key_valid)
+
+
 build_token_metadata = dit_attn_build_token_metadata
+build_key_valid = dit_attn_build_key_valid
 qknorm_rope = dit_attn_qknorm_rope
 forward = dit_attn_forward
 forward_cached = dit_attn_forward_cached

@@ -88,6 +88,30 @@ int dit_attn_build_token_metadata(const uint8_t* image_pad_mask, int32_t seq_len
   return e == hipSuccess ? DIT_ATTN_OK : DIT_ATTN_ERR_HIP;
 }
 
+int dit_attn_build_key_valid(const uint8_t* image_pad_mask, int32_t seq_len, const uint8_t* text_valid,
+                             int32_t B, int32_t n_text, int64_t text_valid_stride, uint64_t* key_valid,
+                             int64_t key_valid_stride, int32_t* status_dev, void* stream) {
+  if (B < 0 || seq_len < 0 || n_text < 0) return DIT_ATTN_ERR_SHAPE;
+  if (B == 0 || seq_len == 0) return DIT_ATTN_OK;  // nothing to do; no pointer is read
+  if (!image_pad_mask || !key_valid || !status_dev || (n_text > 0 && !text_valid)) return DIT_ATTN_ERR_NULL;
+  if (n_text > seq_len || text_valid_stride < n_text) return DIT_ATTN_ERR_SHAPE;
+  if (key_valid_stride < ((int64_t)seq_len + 63) / 64) return DIT_ATTN_ERR_SHAPE;
+  if (B > 65535) return DIT_ATTN_ERR_UNSUPPORTED;
+  if ((reinterpret_cast<uintptr_t>(key_valid) & 7u) != 0) return DIT_ATTN_ERR_ALIGN;
+  dit::KeyValidArgs a{};
+  a.mask = image_pad_mask;
+  a.text_valid = text_valid;
+  a.bits = key_valid;
+  a.status = status_dev;
+  a.tv_stride = text_valid_stride;
+  a.bits_stride = key_valid_stride;
+  a.S = seq_len;
+  a.B = B;
+  a.n_text = n_text;
+  hipError_t e = dit::launch_key_valid(a, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DIT_ATTN_OK : DIT_ATTN_ERR_HIP;
+}
+
 int dit_attn_qknorm_rope(const void* q, const void* k, void* q_out, void* k_out, const void* q_weight,
                          const void* k_weight, int32_t B, int32_t S, int32_t H, int32_t H_kv, int32_t D,
                          const int64_t q_strides[3], const int64_t k_strides[3], const int64_t qo_strides[3],
@@ -158,7 +182,8 @@ int dit_attn_qknorm_rope(const void* q, const void* k, void* q_out, void* k_out,
 static int attention_common(const void* q, const void* kc, const void* vc, const void* kn, const void* vn, void* o,
                             float* lse, int32_t B, int32_t P, int32_t S_new, int32_t H, int32_t H_kv, int32_t D,
                             const int64_t* const st[6], int32_t mask_mode, const dit_attn_token_meta* meta,
-                            float softmax_scale, int32_t dtype, void* stream) {
+                            const uint64_t* key_valid, int64_t key_valid_stride, float softmax_scale,
+                            int32_t dtype, void* stream) {
   if (dtype != DIT_ATTN_BF16 && dtype != DIT_ATTN_F32) return DIT_ATTN_ERR_UNSUPPORTED;
   if (mask_mode != DIT_ATTN_MASK_FULL && mask_mode != DIT_ATTN_MASK_BLOCK_CAUSAL) return DIT_ATTN_ERR_UNSUPPORTED;
   if (B < 0 || P < 0 || S_new < 0 || H < 1 || H_kv < 1 || H % H_kv != 0) return DIT_ATTN_ERR_SHAPE;
@@ -180,6 +205,8 @@ static int attention_common(const void* q, const void* kc, const void* vc, const
       !rows_aligned(o, st[5], es))
     return DIT_ATTN_ERR_ALIGN;
   if (P > 0 && (!rows_aligned(kc, st[1], es) || !rows_aligned(vc, st[2], es))) return DIT_ATTN_ERR_ALIGN;
+  if (key_valid && key_valid_stride < ((int64_t)P + S_new + 63) / 64) return DIT_ATTN_ERR_SHAPE;
+  if (key_valid && (reinterpret_cast<uintptr_t>(key_valid) & 7u) != 0) return DIT_ATTN_ERR_ALIGN;
   if (B == 0 || S_new == 0) return DIT_ATTN_OK;
   // Keys are addressed with 32-bit byte offsets inside one (batch, kv-head) slice.
   const int64_t span_new = (int64_t)S_new * std::max(st[3][1], st[4][1]) * es;
@@ -197,6 +224,8 @@ static int attention_common(const void* q, const void* kc, const void* vc, const
   a.o = o;
   a.lse = lse;
   a.kv_limit = kv_limit;
+  a.key_bits = key_valid;
+  a.kb_stride = key_valid ? key_valid_stride : 0;
   for (int i = 0; i < 3; ++i) {
     a.qs[i] = st[0][i];
     a.kcs[i] = P > 0 ? st[1][i] : st[3][i];
@@ -224,8 +253,20 @@ int dit_attn_forward(const void* q, const void* k, const void* v, void* o, float
   if (B == 0 || S == 0) return DIT_ATTN_OK;  // nothing to do; no pointer is read
   if (!q || !k || !v || !o || !strides) return DIT_ATTN_ERR_NULL;
   const int64_t* st[6] = {strides[0], strides[1], strides[2], strides[1], strides[2], strides[3]};
-  return attention_common(q, k, v, k, v, o, lse, B, 0, S, H, H_kv, D, st, mask_mode, meta, softmax_scale, dtype,
-                          stream);
+  return attention_common(q, k, v, k, v, o, lse, B, 0, S, H, H_kv, D, st, mask_mode, meta, nullptr, 0,
+                          softmax_scale, dtype, stream);
+}
+
+int dit_attn_forward_padded(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B,
+                            int32_t S, int32_t H, int32_t H_kv, int32_t D, const int64_t strides[4][3],
+                            int32_t mask_mode, const dit_attn_token_meta* meta, const uint64_t* key_valid,
+                            int64_t key_valid_stride, float softmax_scale, int32_t dtype, void* stream) {
+  if (B < 0 || S < 0) return DIT_ATTN_ERR_SHAPE;
+  if (B == 0 || S == 0) return DIT_ATTN_OK;  // nothing to do; no pointer is read
+  if (!q || !k || !v || !o || !strides || !key_valid) return DIT_ATTN_ERR_NULL;
+  const int64_t* st[6] = {strides[0], strides[1], strides[2], strides[1], strides[2], strides[3]};
+  return attention_common(q, k, v, k, v, o, lse, B, 0, S, H, H_kv, D, st, mask_mode, meta, key_valid,
+                          key_valid_stride, softmax_scale, dtype, stream);
 }
 
 int dit_attn_forward_cached(const void* q_new, const void* k_cache, const void* v_cache, const void* k_new,
@@ -238,7 +279,21 @@ int dit_attn_forward_cached(const void* q_new, const void* k_cache, const void* 
   if (P > 0 && (!k_cache || !v_cache)) return DIT_ATTN_ERR_NULL;
   const int64_t* st[6] = {strides[0], strides[1], strides[2], strides[3], strides[4], strides[5]};
   return attention_common(q_new, k_cache, v_cache, k_new, v_new, o, lse, B, P, S_new, H, H_kv, D, st, mask_mode,
-                          meta, softmax_scale, dtype, stream);
+                          meta, nullptr, 0, softmax_scale, dtype, stream);
+}
+
+int dit_attn_forward_cached_padded(const void* q_new, const void* k_cache, const void* v_cache, const void* k_new,
+                                   const void* v_new, void* o, float* lse, int32_t B, int32_t P, int32_t S_new,
+                                   int32_t H, int32_t H_kv, int32_t D, const int64_t strides[6][3],
+                                   int32_t mask_mode, const dit_attn_token_meta* meta, const uint64_t* key_valid,
+                                   int64_t key_valid_stride, float softmax_scale, int32_t dtype, void* stream) {
+  if (B < 0 || P < 0 || S_new < 0) return DIT_ATTN_ERR_SHAPE;
+  if (B == 0 || S_new == 0) return DIT_ATTN_OK;  // nothing to do; no pointer is read
+  if (!q_new || !k_new || !v_new || !o || !strides || !key_valid) return DIT_ATTN_ERR_NULL;
+  if (P > 0 && (!k_cache || !v_cache)) return DIT_ATTN_ERR_NULL;
+  const int64_t* st[6] = {strides[0], strides[1], strides[2], strides[3], strides[4], strides[5]};
+  return attention_common(q_new, k_cache, v_cache, k_new, v_new, o, lse, B, P, S_new, H, H_kv, D, st, mask_mode,
+                          meta, key_valid, key_valid_stride, softmax_scale, dtype, stream);
 }
 
 }  // extern "C"

@@ -32,6 +32,11 @@
 //    rescaled and probabilities stay <= 2^8.
 //  * All query tiles of one (batch, head) run on one XCD (and its L2); the
 //    light low query tiles of each XCD go out last.
+//  * Padded text keys (same page, forward's encoder_hidden_states_mask): one
+//    validity word per key tile and sample, read through the scalar cache; a
+//    tile whose word is not all ones takes the per-element mask path.  A row
+//    keeps no offset until its first finite logit, and a row with no valid key
+//    at all ends with O = 0 and lse = -inf.
 
 #include <cmath>
 
@@ -116,7 +121,8 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, char* dst, in
 // MFMA output is the exponent itself.
 // ALIGNED: the cache length P is a multiple of the key tile, so no tile mixes
 // cached and new keys and every tile load comes from one source.
-template <int DP, int NW, bool UNIT, bool ALIGNED>
+// PADDED: a.key_bits marks the valid keys of each sample.
+template <int DP, int NW, bool UNIT, bool ALIGNED, bool PADDED>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   static_assert(DP % 32 == 0 && DP <= 128, "padded head dim");
   constexpr int KSTEPS = DP / 16;  // QK^T contraction steps
@@ -144,6 +150,19 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   const int kvh = h / (a.H / a.Hk);
   const int Sk = a.Sk;
   const int P = a.P;
+
+  // Validity word of key tile t for this sample (all ones without padding).
+  // The constant address space lets the uniform load go through the scalar
+  // cache, outside the vector-memory counts the tile waits rely on; volatile
+  // keeps it where it is written (before a tile barrier, whose wait then
+  // covers its latency) instead of next to its use.
+  using const_u64 = const volatile __attribute__((address_space(4))) uint64_t;
+  const_u64* kbits = nullptr;
+  if constexpr (PADDED) kbits = (const_u64*)(a.key_bits + (int64_t)b * a.kb_stride);
+  auto tile_word = [&](int t) __attribute__((always_inline)) -> uint64_t {
+    if constexpr (PADDED) return kbits[t];
+    return ~0ull;
+  };
 
   // This lane's query row and its key bound.
   const int qrow = qtile * 32 * NW + wave * 32 + (lane & 31);
@@ -283,7 +302,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   const float c2 = a.scale * 1.4426950408889634f;  // scale * log2(e); 1 when UNIT
   const float ic2 = UNIT ? 1.0f : 1.0f / c2;
   float m_off = 0.f;   // running offset (log2 units)
-  bool fresh = true;   // no tile seen yet: the first one sets the offset
+  bool fresh = true;   // no finite logit seen yet: the first one sets the offset
   float l_part = 0.f;  // this lane's share of the row sum
 
   // S^T (logits minus the offset, logit units) for the 64 keys of a K stage.
@@ -302,15 +321,19 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
       }
     }
   };
-  // Mask keys >= this row's bound (only tiles that reach past a wave's smallest bound).
-  auto mask = [&](int t, f32x16 (&sacc)[2]) __attribute__((always_inline)) {
+  // Mask keys >= this row's bound and keys whose validity bit is 0 (only
+  // tiles that reach past a wave's smallest bound or hold a padded key).
+  auto mask = [&](int t, f32x16 (&sacc)[2], uint64_t word) __attribute__((always_inline)) {
     const int k0 = t * kTileN;
+    const uint64_t wl = word >> (4 * g);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int key = k0 + 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
-        if (key >= lim) sacc[kb][i] = -INFINITY;
+        const int j = 32 * kb + 8 * (i >> 2) + (i & 3);  // key within the tile, less 4g
+        bool off = k0 + j + 4 * g >= lim;
+        if constexpr (PADDED) off = off || ((wl >> j) & 1) == 0;
+        if (off) sacc[kb][i] = -INFINITY;
       }
   };
   auto rowmax = [&](const f32x16 (&sacc)[2]) __attribute__((always_inline)) {
@@ -336,7 +359,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
       for (int kb = 0; kb < 2; ++kb) sacc[kb] -= d;
       m_off += d * c2;
     }
-    fresh = false;
+    // Without padding every row's first tile holds key 0, which it may see.
+    if constexpr (PADDED)
+      fresh = fresh && !(mx > -INFINITY);
+    else
+      fresh = false;
   };
   // P = exp2(c2 * S) as bf16 B operands; row sums from the same bf16 values.
   auto softmax = [&](const f32x16 (&sacc)[2], bf16x8 (&pop)[2][2]) __attribute__((always_inline)) {
@@ -412,15 +439,17 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
       }
     }
   };
-  auto phase2 = [&](int t, const char* v_cur, f32x16 (&s_nxt)[2]) __attribute__((always_inline)) {
+  // wn: validity word of tile t + 1 (loaded before the barrier that opens
+  // the phase, so the barrier wait covers its latency).
+  auto phase2 = [&](int t, const char* v_cur, f32x16 (&s_nxt)[2], uint64_t wn) __attribute__((always_inline)) {
     const int k0 = t * kTileN;
     if (k0 >= wlim_max) return;
     const int k1 = k0 + kTileN;
     const bool has_next = k1 < wlim_max && k1 < Sk;
     if (has_next) {
-      if (k1 + kTileN > wlim_min) {
+      if (k1 + kTileN > wlim_min || wn != ~0ull) {
         pv(v_cur, pop);
-        mask(t + 1, s_nxt);
+        mask(t + 1, s_nxt, wn);
         mx_cur = rowmax(s_nxt);
       } else {
         pv(v_cur, pop);
@@ -471,28 +500,35 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   qk(sK0, sA);
-  if (kTileN > wlim_min) mask(0, sA);
+  {
+    const uint64_t w0 = tile_word(0);
+    if (kTileN > wlim_min || w0 != ~0ull) mask(0, sA, w0);
+  }
   mx_cur = rowmax(sA);
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
   __builtin_amdgcn_s_barrier();  // every wave is done with K(0)
   asm volatile("" ::: "memory");
   issue(2, sK0, true);
 
-  // Stages are named statically, two iterations per trip.
+  // Stages are named statically, two iterations per trip.  The validity word
+  // of a tile past the last one is never used; its index stays in the row.
+  const int last_tile = (Sk - 1) / kTileN;
   for (int t = 0; t < n_tiles; t += 2) {
     wait_tile();  // K(t+1) in sK1; sV1 (V(t-1)) read by every wave
     issue(t + 1, sV1, false);
     phase1(t, sK1, sA, sB);
+    const uint64_t w1 = tile_word(min(t + 1, last_tile));
     wait_tile();  // V(t) in sV0; sK1 (K(t+1)) read by every wave
     issue(t + 3, sK1, true);
-    phase2(t, sV0, sB);
+    phase2(t, sV0, sB, w1);
     if (t + 1 >= n_tiles) break;
     wait_tile();  // K(t+2) in sK0; sV0 (V(t)) read by every wave
     issue(t + 2, sV0, false);
     phase1(t + 1, sK0, sB, sA);
+    const uint64_t w2 = tile_word(min(t + 2, last_tile));
     wait_tile();  // V(t+1) in sV1; sK0 (K(t+2)) read by every wave
     issue(t + 4, sK0, true);
-    phase2(t + 1, sV1, sA);
+    phase2(t + 1, sV1, sA, w2);
   }
   // Tiles past the last one were issued too: drain before the work-group's
   // LDS can be handed to another.
@@ -501,7 +537,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   // Normalise and store: lane holds query (lane & 31), channels
   // 32*mb + 8*(i/4) + 4*g + (i%4).
   const float l_tot = sum_with_partner32(l_part);
-  const float inv = 1.0f / l_tot;
+  const bool empty = PADDED && !(l_tot > 0.f);  // no valid key: O = 0, lse = -inf
+  const float inv = empty ? 0.f : 1.0f / l_tot;
   if (row_ok) {
     __bf16* op = reinterpret_cast<__bf16*>(a.o) + b * a.os[0] + (int64_t)qrow * a.os[1] + h * a.os[2];
 #pragma unroll
@@ -518,7 +555,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
       }
     }
     if (a.lse != nullptr && g == 0)
-      a.lse[((int64_t)b * a.H + h) * a.Snew + qrow] = (m_off + __log2f(l_tot)) * 0.6931471805599453f;
+      a.lse[((int64_t)b * a.H + h) * a.Snew + qrow] =
+          empty ? -INFINITY : (m_off + __log2f(l_tot)) * 0.6931471805599453f;
   }
 }
 
@@ -540,6 +578,7 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(AttnArgs a) {
   const bool row_ok = qrow < a.Snew;
   const int qclamp = row_ok ? qrow : a.Snew - 1;
   const int lim = a.kv_limit ? a.kv_limit[a.P + qclamp] : a.Sk;
+  const uint64_t* kbits = a.key_bits ? a.key_bits + (int64_t)b * a.kb_stride : nullptr;
   int wlim = lim;
   for (int m = 32; m >= 1; m >>= 1) wlim = max(wlim, __shfl_xor(wlim, m, 64));
 
@@ -574,12 +613,14 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(AttnArgs a) {
     __syncthreads();
     float s[TK];
     float mx = -INFINITY;
+    // Validity of keys k0 .. k0 + 31 (one half of a 64-key word).
+    const uint32_t vbits = kbits ? (uint32_t)(kbits[k0 >> 6] >> (k0 & 63)) : 0xffffffffu;
 #pragma unroll
     for (int j = 0; j < TK; ++j) {
       float acc = 0.f;
 #pragma unroll
       for (int d = 0; d < DP; ++d) acc = fmaf(q[d], sk[j][d], acc);
-      s[j] = (k0 + j < lim) ? acc * a.scale : -INFINITY;
+      s[j] = (k0 + j < lim && ((vbits >> j) & 1u)) ? acc * a.scale : -INFINITY;
       mx = fmaxf(mx, s[j]);
     }
     const float m_new = fmaxf(m_cur, mx);
@@ -600,29 +641,40 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(AttnArgs a) {
   }
   if (row_ok) {
     float* op = reinterpret_cast<float*>(a.o) + b * a.os[0] + (int64_t)qrow * a.os[1] + h * a.os[2];
-    const float inv = 1.0f / l;
+    // A row with no valid key (padding) has l = 0: O = 0, lse = -inf.
+    const float inv = l > 0.f ? 1.0f / l : 0.f;
     for (int d = 0; d < a.D; ++d) op[d] = o[d] * inv;
-    if (a.lse != nullptr) a.lse[((int64_t)b * a.H + h) * a.Snew + qrow] = m_cur + logf(l);
+    if (a.lse != nullptr) a.lse[((int64_t)b * a.H + h) * a.Snew + qrow] = l > 0.f ? m_cur + logf(l) : -INFINITY;
   }
+}
+
+constexpr int kWaves = 4;
+
+template <int DP, bool UNIT, bool ALIGNED>
+void launch_bf16_variant(const AttnArgs& a, dim3 grid, hipStream_t stream) {
+  const dim3 block(kWaves * 64);
+  if (a.key_bits != nullptr)
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<DP, kWaves, UNIT, ALIGNED, true>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<DP, kWaves, UNIT, ALIGNED, false>), grid, block, 0, stream, a);
 }
 
 template <int DP>
 hipError_t launch_bf16(const AttnArgs& a, hipStream_t stream) {
-  constexpr int NW = 4;
-  const int n_qtiles = (a.Snew + 32 * NW - 1) / (32 * NW);
+  const int n_qtiles = (a.Snew + 32 * kWaves - 1) / (32 * kWaves);
   const long long nblocks = (long long)n_qtiles * a.B * a.H;
   // Q pre-scaled by scale * log2(e): the scale argument is ln 2 (to rounding).
   const bool unit = std::fabs((double)a.scale * 1.4426950408889634 - 1.0) < 1e-6;
   const bool aligned = a.P % 64 == 0;
-  const dim3 grid((unsigned)nblocks), block(NW * 64);
+  const dim3 grid((unsigned)nblocks);
   if (unit && aligned)
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<DP, NW, true, true>), grid, block, 0, stream, a);
+    launch_bf16_variant<DP, true, true>(a, grid, stream);
   else if (unit)
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<DP, NW, true, false>), grid, block, 0, stream, a);
+    launch_bf16_variant<DP, true, false>(a, grid, stream);
   else if (aligned)
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<DP, NW, false, true>), grid, block, 0, stream, a);
+    launch_bf16_variant<DP, false, true>(a, grid, stream);
   else
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<DP, NW, false, false>), grid, block, 0, stream, a);
+    launch_bf16_variant<DP, false, false>(a, grid, stream);
   return hipGetLastError();
 }
 

@@ -22,6 +22,18 @@ struct TokenMetaArgs {
 hipError_t launch_token_meta(const uint8_t* mask, const TokenMetaArgs& a, int32_t* image_ids, uint8_t* target,
                              int32_t* pos, int32_t* kv_limit, int32_t* status, hipStream_t stream);
 
+// Per-sample key validity bits of the joint sequence from a text mask.
+struct KeyValidArgs {
+  const uint8_t* mask;        // [S] nonzero on image tokens
+  const uint8_t* text_valid;  // [B][n_text], row stride tv_stride bytes
+  uint64_t* bits;             // [B][bits_stride] words; bit j of word t: key 64 t + j
+  int32_t* status;
+  int64_t tv_stride, bits_stride;
+  int32_t S, B, n_text;
+};
+
+hipError_t launch_key_valid(const KeyValidArgs& a, hipStream_t stream);
+
 // Fused QK-RMSNorm + rotary embedding.
 constexpr int kMaxPairs = 64;  // head_dim <= 128
 
@@ -55,6 +67,8 @@ struct AttnArgs {
   void* o;
   float* lse;                // nullable
   const int32_t* kv_limit;   // logical-sequence bound per token; null for the full mask
+  const uint64_t* key_bits;  // nullable: per-sample key validity, bit j of word t = key 64 t + j
+  int64_t kb_stride;         // words per sample of key_bits
   int64_t qs[3], kcs[3], vcs[3], kns[3], vns[3], os[3];
   int32_t B, H, Hk, D, P, Snew, Sk;
   float scale;               // softmax scale

@@ -175,7 +175,66 @@ __global__ __launch_bounds__(kThreads) void token_meta_kernel(const uint8_t* __r
   if (tid == 0) status[0] = s_bad ? 5 : 0;
 }
 
+// Key validity of the joint sequence for one sample per work-group
+// (QwenImage21Transformer2DModel API page, forward's encoder_hidden_states_mask:
+// padded text tokens take no part in attention).  Text token s is the
+// (s - r)-th text token, r being the image tokens before it, and takes that
+// entry of the sample's text mask; image tokens are always valid.  Same
+// segment scan as the metadata kernel; each 64-token group becomes one ballot
+// word, stored by its first lane.  Bits past the sequence end are 0.
+__global__ __launch_bounds__(kThreads) void key_valid_kernel(KeyValidArgs a) {
+  __shared__ int s_wave_cnt[kWaves];
+  __shared__ int s_carry;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int S = a.S;
+  const uint8_t* __restrict__ mask = a.mask;
+  const uint8_t* __restrict__ tv = a.text_valid + (int64_t)blockIdx.x * a.tv_stride;
+  uint64_t* __restrict__ out = a.bits + (int64_t)blockIdx.x * a.bits_stride;
+  if (tid == 0) s_carry = 0;
+  __syncthreads();
+  for (int base = 0; base < S; base += kPass) {
+    const int seg = base + wave * kSeg;
+    bool m[TPT];
+    int cnt = 0;
+#pragma unroll
+    for (int it = 0; it < TPT; ++it) {
+      const int s = seg + it * 64 + lane;
+      m[it] = s < S && mask[s] != 0;
+      cnt += m[it] ? 1 : 0;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off, 64);
+    if (lane == 0) s_wave_cnt[wave] = cnt;
+    __syncthreads();
+    int r0 = s_carry;  // image tokens before this segment
+    for (int w = 0; w < wave; ++w) r0 += s_wave_cnt[w];
+#pragma unroll
+    for (int it = 0; it < TPT; ++it) {
+      const int s = seg + it * 64 + lane;
+      const uint64_t img = __ballot(m[it]);
+      const int j = s - (r0 + lanes_below(img));  // text ordinal of a text token
+      bool valid = m[it];
+      if (s < S && !m[it] && j < a.n_text) valid = tv[j] != 0;
+      const uint64_t word = __ballot(valid);
+      if (lane == 0 && seg + it * 64 < S) out[(seg + it * 64) >> 6] = word;
+      r0 += __builtin_popcountll(img);
+    }
+    __syncthreads();
+    if (tid == kThreads - 1) s_carry = r0;
+    __syncthreads();
+  }
+  // Every work-group sees the same layout; the first reports it.
+  if (blockIdx.x == 0 && tid == 0) a.status[0] = (S - s_carry == a.n_text) ? 0 : 5;
+}
+
 }  // namespace
+
+hipError_t launch_key_valid(const KeyValidArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(key_valid_kernel, dim3((unsigned)a.B), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_token_meta(const uint8_t* mask, const TokenMetaArgs& a, int32_t* image_ids, uint8_t* target,
                              int32_t* pos, int32_t* kv_limit, int32_t* status, hipStream_t stream) {

@@ -16,7 +16,10 @@
  *   4. the same attention with the keys/values of the timestep-independent
  *      prefix (text and condition images) taken from a cache
  *      (QwenImage21Transformer2DModel API page, causal_condition and
- *      forward's kv_cache / kv_cache_mode).
+ *      forward's kv_cache / kv_cache_mode);
+ *   5. either attention with padded text keys left out, per sample
+ *      (QwenImage21Transformer2DModel API page, forward's
+ *      encoder_hidden_states_mask).
  *
  * Conventions shared by every entry point
  *   - Memory: every pointer marked "device" is device memory owned by the
@@ -115,6 +118,31 @@ int dit_attn_build_token_metadata(const uint8_t *image_pad_mask, int32_t seq_len
                                   const dit_attn_token_meta *meta, int32_t *status_dev,
                                   void *stream);
 
+/* Key validity of the joint sequence, per sample, from the text mask
+ * (QwenImage21Transformer2DModel API page, forward's encoder_hidden_states_mask:
+ * a [batch, text length] mask of the valid text tokens; padded ones take no part
+ * in attention).  The j-th text token of the sequence (counting, in sequence
+ * order, the tokens where image_pad_mask is 0) takes entry j of its sample's
+ * text mask; image tokens are always valid.
+ *   image_pad_mask     device uint8 [seq_len], nonzero on image tokens (the
+ *                      metadata's input; shared by the batch).
+ *   text_valid         device uint8 [B][n_text] (row stride text_valid_stride
+ *                      bytes, >= n_text), nonzero = valid.  May be NULL when
+ *                      n_text == 0.
+ *   key_valid          device uint64 [B][key_valid_stride], 8-byte aligned,
+ *                      key_valid_stride >= ceil(seq_len / 64): bit j of word t of
+ *                      sample b is 1 iff key 64 t + j may be attended.  Words
+ *                      0 .. ceil(seq_len / 64) - 1 are written, bits past seq_len
+ *                      as 0; later words are left untouched.
+ *   status_dev         device int32 [1]; receives DIT_ATTN_OK, or DIT_ATTN_ERR_DATA
+ *                      when the mask has a number of text tokens other than
+ *                      n_text (the bits are then unspecified).
+ * B == 0 or seq_len == 0 returns DIT_ATTN_OK at once.  Host-side errors: NULL
+ * pointers, negative sizes, n_text > seq_len, a short stride, B > 65535. */
+int dit_attn_build_key_valid(const uint8_t *image_pad_mask, int32_t seq_len, const uint8_t *text_valid,
+                             int32_t B, int32_t n_text, int64_t text_valid_stride, uint64_t *key_valid,
+                             int64_t key_valid_stride, int32_t *status_dev, void *stream);
+
 /* Fused per-head RMSNorm + multi-axis rotary embedding of Q and K
  * (NucleusMoE-Image pipeline article, section 6.3: qk_norm then rotary;
  *  Lumina-Next DiT article: 2D rotary needs head_dim % 4 == 0).
@@ -179,6 +207,34 @@ int dit_attn_forward_cached(const void *q_new, const void *k_cache, const void *
                             int32_t D, const int64_t strides[6][3], int32_t mask_mode,
                             const dit_attn_token_meta *meta, float softmax_scale,
                             int32_t dtype, void *stream);
+
+/* dit_attn_forward with padded keys left out (QwenImage21Transformer2DModel API
+ * page, forward's encoder_hidden_states_mask): query q of sample b attends the
+ * keys that the mask mode allows AND whose bit in key_valid is 1.
+ *   key_valid         device uint64 [B][key_valid_stride] as written by
+ *                     dit_attn_build_key_valid (any bits may be passed), 8-byte
+ *                     aligned, key_valid_stride >= ceil(S / 64) words.
+ * A query with no allowed valid key gets O = 0 and lse = -inf.  K and V must be
+ * finite at padded keys too (they enter as probability 0 times the value).
+ * With every bit of keys 0 .. S-1 set, the result is bit-identical to
+ * dit_attn_forward.  Other arguments and errors as dit_attn_forward. */
+int dit_attn_forward_padded(const void *q, const void *k, const void *v, void *o, float *lse,
+                            int32_t B, int32_t S, int32_t H, int32_t H_kv, int32_t D,
+                            const int64_t strides[4][3], int32_t mask_mode,
+                            const dit_attn_token_meta *meta, const uint64_t *key_valid,
+                            int64_t key_valid_stride, float softmax_scale, int32_t dtype,
+                            void *stream);
+
+/* dit_attn_forward_cached with padded keys left out: bits index the logical
+ * sequence (cache keys 0 .. P-1, then the new keys), key_valid_stride >=
+ * ceil((P + S_new) / 64).  Otherwise as dit_attn_forward_padded. */
+int dit_attn_forward_cached_padded(const void *q_new, const void *k_cache, const void *v_cache,
+                                   const void *k_new, const void *v_new, void *o, float *lse,
+                                   int32_t B, int32_t P, int32_t S_new, int32_t H, int32_t H_kv,
+                                   int32_t D, const int64_t strides[6][3], int32_t mask_mode,
+                                   const dit_attn_token_meta *meta, const uint64_t *key_valid,
+                                   int64_t key_valid_stride, float softmax_scale, int32_t dtype,
+                                   void *stream);
 
 /* Static description of a status code (never NULL). */
 const char *dit_attn_status_string(int32_t status);

@@ -129,3 +129,48 @@ def test_empty_inputs_are_noops():
                                      None) == _lib.OK
     assert _lib.lib.dit_attn_forward(FAKE, FAKE, FAKE, FAKE2, None, 2, 0, 32, 32, 128, st4, 0, None, 0.0, 0,
                                      None) == _lib.OK
+
+
+def test_key_valid_argument_errors():
+    from diffusion_transformer_joint_token_amd import _lib
+    f = _lib.lib.dit_attn_build_key_valid
+
+    def call(mask=FAKE, S=5120, tv=FAKE, B=2, n_text=1024, tv_stride=1024, bits=FAKE2, words=80, status=FAKE):
+        return f(mask, S, tv, B, n_text, tv_stride, bits, words, status, None)
+    assert call(mask=None) == _lib.ERR_NULL
+    assert call(tv=None) == _lib.ERR_NULL
+    assert call(bits=None) == _lib.ERR_NULL
+    assert call(status=None) == _lib.ERR_NULL
+    assert call(n_text=5121) == _lib.ERR_SHAPE          # more text tokens than the sequence
+    assert call(tv_stride=1000) == _lib.ERR_SHAPE       # rows overlap
+    assert call(words=79) == _lib.ERR_SHAPE             # 5120 keys need 80 words
+    assert call(n_text=-1) == _lib.ERR_SHAPE
+    assert call(bits=FAKE2 + 4) == _lib.ERR_ALIGN
+    assert call(B=70000) == _lib.ERR_UNSUPPORTED
+    assert call(B=0, mask=None) == _lib.OK              # empty: nothing read
+    assert call(S=0, mask=None) == _lib.OK
+
+
+def test_padded_attention_argument_errors():
+    from diffusion_transformer_joint_token_amd import _lib
+    f = _lib.lib.dit_attn_forward_padded
+    st4 = (_lib.Strides3 * 4)(*[_s3(5120 * 4096, 4096, 128)] * 4)
+    m = _meta(5120)
+
+    def call(q=FAKE, kb=FAKE2, words=80, S=5120, B=2):
+        return f(q, FAKE, FAKE, FAKE2, None, B, S, 32, 32, 128, st4, 1, ctypes.byref(m), kb, words, 0.0, 0, None)
+    assert call(kb=None) == _lib.ERR_NULL
+    assert call(q=None) == _lib.ERR_NULL
+    assert call(words=79) == _lib.ERR_SHAPE
+    assert call(kb=FAKE2 + 4) == _lib.ERR_ALIGN
+    assert call(S=5000, words=80) == _lib.ERR_SHAPE     # metadata length mismatch
+    assert call(B=0, q=None) == _lib.OK
+    fc = _lib.lib.dit_attn_forward_cached_padded
+    st6 = (_lib.Strides3 * 6)(*[_s3(5120 * 4096, 4096, 128)] * 6)
+
+    def callc(kb=FAKE2, words=2, kc=FAKE):
+        return fc(FAKE, kc, FAKE, FAKE, FAKE, FAKE2, None, 1, 16, 100, 32, 32, 128, st6, 1,
+                  ctypes.byref(_meta(116)), kb, words, 0.0, 0, None)
+    assert callc(kb=None) == _lib.ERR_NULL
+    assert callc(kc=None) == _lib.ERR_NULL
+    assert callc(words=1) == _lib.ERR_SHAPE             # 116 logical keys need 2 words

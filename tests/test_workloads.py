@@ -34,3 +34,18 @@ def test_draw_is_seeded_and_prefix_stable():
     assert np.array_equal(a.bits["v"], b.bits["v"])
     assert a.bits["q"].dtype == np.uint16 and a.vals["q"].dtype == np.float64
     assert a.vals["q"].shape == (1, 7, 2, 8) and a.vals["k"].shape == (1, 7, 1, 8)
+
+
+def test_text_mask_recipes():
+    w = wl.get("qwen_image21_t1024_i64x64")
+    assert wl.n_text_tokens(w) == 1024
+    a = wl.text_mask(w, 3, "right")
+    assert a.shape == (2, 1024) and a.dtype == np.uint8
+    assert np.array_equal(a, wl.text_mask(w, 3, "right"))
+    for row in a:  # a valid prefix, then padding
+        L = int(row.sum())
+        assert L >= 1 and np.all(row[:L] == 1) and np.all(row[L:] == 0)
+    r = wl.text_mask(w, 4, "random")
+    assert set(np.unique(r)) <= {0, 1} and 0.4 < r.mean() < 0.6
+    assert wl.text_mask(w, 5, "none").all()
+    assert wl.text_mask(wl.get("lumina_next_full_gqa"), 1, "right").shape == (2, 0)

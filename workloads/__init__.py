@@ -26,7 +26,7 @@ from typing import Dict, List, Sequence, Tuple
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "get", "sequence_inputs", "draw", "bf16_round_bits",
-           "bf16_bits_to_f64", "small_workload"]
+           "bf16_bits_to_f64", "small_workload", "n_text_tokens", "text_mask"]
 
 
 @dataclass(frozen=True)
@@ -119,6 +119,32 @@ def sequence_inputs(w: Workload) -> Tuple[np.ndarray, List[Tuple[int, int, int]]
             mask += [1] * (f * h * wd)
             shapes.append((f, h, wd))
     return np.asarray(mask, dtype=np.uint8), shapes
+
+
+def n_text_tokens(w: Workload) -> int:
+    return sum(seg[1] for seg in w.layout if seg[0] == "T")
+
+
+def text_mask(w: Workload, seed: int, kind: str = "right", min_valid: int = 1) -> np.ndarray:
+    """Seeded per-sample text masks, uint8 [batch, text tokens], 1 = valid.
+
+    "right": a tokenizer's padding -- sample b keeps its first L_b text tokens,
+      L_b uniform in [min_valid, n_text] (default_rng(seed).integers);
+    "random": every entry an independent fair coin (patterns no tokenizer
+      makes, for the masking logic itself);
+    "none": all valid."""
+    n = n_text_tokens(w)
+    out = np.ones((w.batch, n), dtype=np.uint8)
+    rng = np.random.default_rng(seed)
+    if kind == "right":
+        for b in range(w.batch):
+            L = int(rng.integers(min(min_valid, n), n + 1))
+            out[b, L:] = 0
+    elif kind == "random":
+        out = rng.integers(0, 2, size=(w.batch, n)).astype(np.uint8)
+    elif kind != "none":
+        raise ValueError(kind)
+    return out
 
 
 def bf16_round_bits(x: np.ndarray) -> np.ndarray:
