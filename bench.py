@@ -46,11 +46,25 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def useful_pairs(kv_limit: np.ndarray, w: wl.Workload) -> int:
-    """Allowed (q, k) pairs per (batch, head) for the workload's query rows."""
-    if w.mask_mode == "full":
-        return w.n_new * w.seq_len
-    return int(kv_limit[w.prefix_len:].astype(np.int64).sum())
+def useful_pairs(kv_limit: np.ndarray, w: wl.Workload, valid_keys=None) -> int:
+    """Allowed (q, k) pairs summed over the batch, per head, for the workload's
+    query rows; with valid_keys (bool [B, S]) padded keys are not counted."""
+    lim = (np.full(w.n_new, w.seq_len, dtype=np.int64) if w.mask_mode == "full"
+           else kv_limit[w.prefix_len:].astype(np.int64))
+    if valid_keys is None:
+        return int(lim.sum()) * w.batch
+    below = np.concatenate([np.zeros((w.batch, 1), np.int64), np.cumsum(valid_keys, axis=1)], axis=1)
+    return int(below[:, lim].sum())
+
+
+def text_valid_keys(mask: np.ndarray, tv: np.ndarray) -> np.ndarray:
+    """bool [B, S] for the FLOP count: image tokens, and text tokens whose
+    entry (by text ordinal) in the sample's text mask is set."""
+    text = mask == 0
+    ordinal = np.cumsum(text) - 1
+    out = np.ones((tv.shape[0], mask.size), dtype=bool)
+    out[:, text] = tv[:, ordinal[text]] != 0
+    return out
 
 
 def source_sha(path: str) -> str:
@@ -74,7 +88,7 @@ def measured_traffic(w: wl.Workload):
 class Step:
     """Device buffers and the launch sequence of one step."""
 
-    def __init__(self, w: wl.Workload, device):
+    def __init__(self, w: wl.Workload, device, text_padding: str = "none"):
         import torch
         import diffusion_transformer_joint_token_amd as dit
         self.torch, self.dit, self.w = torch, dit, w
@@ -93,6 +107,14 @@ class Step:
         mask, self.shapes = wl.sequence_inputs(w)
         self.mask = torch.from_numpy(mask).to(device)
         self.meta = dit.TokenMeta.empty(w.seq_len, device)
+        # Padded text: a seeded per-sample text mask; its key-validity bits are
+        # rebuilt with the metadata every step and passed to the attention.
+        self.tv, self.kv, self.tv_dev = None, None, None
+        if text_padding != "none":
+            self.tv = wl.text_mask(w, 2024, text_padding)
+            self.tv_dev = torch.from_numpy(self.tv).to(device)
+            self.kv = dit.KeyValid(torch.empty(w.batch, (w.seq_len + 63) // 64, dtype=torch.int64, device=device),
+                                   torch.empty(1, dtype=torch.int32, device=device))
         self.qp = torch.empty_like(self.q)
         self.kp = torch.empty_like(self.k)
         self.o = torch.empty_like(self.q)
@@ -100,6 +122,8 @@ class Step:
 
     def metadata(self):
         self.dit.build_token_metadata(self.mask, self.shapes, self.w.pos_mode, out=self.meta)
+        if self.kv is not None:
+            self.dit.build_key_valid(self.mask, self.tv_dev, out=self.kv)
 
     def norm_rope(self):
         # The softmax scale and log2(e) are folded into Q' here (one rounding),
@@ -111,10 +135,10 @@ class Step:
     def attention(self):
         if self.w.prefix_len:
             self.dit.forward_cached(self.qp, self.kc, self.vc, self.kp, self.v, self.w.mask_mode, self.meta,
-                                    softmax_scale=self.dit.LN2, out=self.o)
+                                    softmax_scale=self.dit.LN2, out=self.o, key_valid=self.kv)
         else:
             self.dit.forward(self.qp, self.kp, self.v, self.w.mask_mode, self.meta, softmax_scale=self.dit.LN2,
-                             out=self.o)
+                             out=self.o, key_valid=self.kv)
 
     def run(self):
         self.metadata()
@@ -204,7 +228,7 @@ def multistep(step: Step, n_steps: int, reps: int, warmup: int, full_ms: float):
         dit.qknorm_rope(q_new, k_new, step.meta.pos_ids[P:], w.axes, w.eps, step.wq, step.wk,
                         q_out=qp_new, k_out=kp_new, q_scale=scale)
         dit.forward_cached(qp_new, k_cache, v_cache, kp_new, v_new, w.mask_mode, step.meta,
-                           softmax_scale=dit.LN2, out=o_new)
+                           softmax_scale=dit.LN2, out=o_new, key_valid=step.kv)
     step.run()
     for _ in range(warmup):
         cached()
@@ -223,11 +247,13 @@ def multistep(step: Step, n_steps: int, reps: int, warmup: int, full_ms: float):
             "cached_rows_equal_full_rows": same}
 
 
-def cpu_baseline(w: wl.Workload, drawn: wl.Drawn, budget_s: float = 12.0):
+def cpu_baseline(w: wl.Workload, drawn: wl.Drawn, budget_s: float = 12.0, text_valid=None):
     """The fp64 oracle (as it stands) on the host: norm + rope of the sampled
     query rows, then their attention rows; rows drawn at random from the
-    workload until the time budget is used.  Scaled to the useful FLOP rate."""
+    workload until the time budget is used.  Scaled to the useful FLOP rate
+    (with a text mask: padded keys left out and not counted)."""
     import oracle.attention as oatt
+    import oracle.key_padding as okp
     import oracle.metadata as ometa
     import oracle.qknorm_rope as oqr
     try:
@@ -243,6 +269,9 @@ def cpu_baseline(w: wl.Workload, drawn: wl.Drawn, budget_s: float = 12.0):
     kp = oqr.qknorm_rope(drawn.vals["k"], drawn.vals["wk"], w.eps, pos, w.axes)
     k_all = np.concatenate([drawn.vals["k_cache"], kp], axis=1) if P else kp
     v_all = np.concatenate([drawn.vals["v_cache"], drawn.vals["v"]], axis=1) if P else drawn.vals["v"]
+    valid = okp.joint_key_valid(mask, text_valid) if text_valid is not None else None
+    below = (np.concatenate([np.zeros((w.batch, 1), np.int64), np.cumsum(valid, axis=1)], axis=1)
+             if valid is not None else None)
     rng = np.random.default_rng(0)
     rows_done, pairs = 0, 0
     chunk = 64
@@ -250,12 +279,13 @@ def cpu_baseline(w: wl.Workload, drawn: wl.Drawn, budget_s: float = 12.0):
         rows = np.sort(rng.choice(w.n_new, size=chunk, replace=False))
         qp = oqr.qknorm_rope(drawn.vals["q"][:, rows], drawn.vals["wq"], w.eps, pos[rows], w.axes)
         for j, r in enumerate(rows):
-            oatt.attention(qp[:, j:j + 1], k_all, v_all, md["image_ids"], w.mask_mode, q_offset=P + int(r))
+            oatt.attention(qp[:, j:j + 1], k_all, v_all, md["image_ids"], w.mask_mode, q_offset=P + int(r),
+                           key_valid=valid)
         rows_done += rows.size
         lim = md["kv_limit"][P + rows] if w.mask_mode == "block_causal" else np.full(rows.size, w.seq_len)
-        pairs += int(lim.sum())
+        pairs += int(lim.sum()) * w.batch if below is None else int(below[:, lim].sum())
     elapsed = time.perf_counter() - t0
-    flops = 4.0 * w.head_dim * pairs * w.heads * w.batch
+    flops = 4.0 * w.head_dim * pairs * w.heads
     return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": "%d random query rows (all %d heads x batch %d) of %s incl. K norm+rope of every token; "
                       "%.1f s wall" % (rows_done, w.heads, w.batch, w.name, elapsed),
@@ -330,6 +360,9 @@ def main(argv=None) -> int:
                          "target block against the cached prefix K/V; adds a 'multistep' object to the line")
     ap.add_argument("--shard-heads", type=int, default=1, metavar="K",
                     help="run one GPU's share of a K-way head-sharded job: heads and kv_heads divided by K")
+    ap.add_argument("--text-padding", default="none", choices=["none", "right", "random"],
+                    help="pad the text per sample (seeded text mask: 'right' keeps a random-length prefix, "
+                         "'random' a coin per token) and run the padded attention entry points")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (the reference "
@@ -367,16 +400,26 @@ def main(argv=None) -> int:
             return 2
         w = dataclasses.replace(w, name="%s_heads_div%d" % (w.name, K), heads=w.heads // K,
                                 kv_heads=w.kv_heads // K)
+    if args.text_padding != "none":
+        if wl.n_text_tokens(w) == 0:
+            print("--text-padding needs a workload with text tokens", file=sys.stderr)
+            return 2
+        w = dataclasses.replace(w, name="%s_textpad_%s" % (w.name, args.text_padding))
     log("workload %s: B=%d H=%d/%d D=%d S=%d (queries %d) mask=%s dtype=%s" % (
         w.name, w.batch, w.heads, w.kv_heads, w.head_dim, w.seq_len, w.n_new, w.mask_mode, w.dtype))
-    step = Step(w, "cuda")
+    step = Step(w, "cuda", args.text_padding)
     step.run()
     torch.cuda.synchronize()
     step.meta.check()
+    valid = None
+    if step.kv is not None:
+        step.kv.check()
+        valid = text_valid_keys(wl.sequence_inputs(w)[0], step.tv)
+        log("valid text tokens per sample: %s of %d" % (step.tv.sum(axis=1).tolist(), step.tv.shape[1]))
     kv_limit = step.meta.kv_limit.cpu().numpy()
-    pairs = useful_pairs(kv_limit, w)
-    flops = 4.0 * w.head_dim * pairs * w.heads * w.batch
-    log("useful pairs per (b,h) %d  useful FLOPs/step %.4e" % (pairs, flops))
+    pairs = useful_pairs(kv_limit, w, valid)
+    flops = 4.0 * w.head_dim * pairs * w.heads
+    log("useful pairs per head (batch summed) %d  useful FLOPs/step %.4e" % (pairs, flops))
 
     t = time_gpu(step, args.steps, args.warmup)
     log("timing: %s" % json.dumps(t))
@@ -390,7 +433,7 @@ def main(argv=None) -> int:
 
     roofline = {"bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": attn_tflops / PEAK_BF16_TFLOPS, "traffic": measured_traffic(w),
-                "kernel": "attn_fwd_bf16_kernel<128,4>", "launch_ms_mean": t["attn_ms_mean"],
+                "kernel": "attn_fwd_bf16_kernel<128,4%s>" % (",padded" if step.kv is not None else ""), "launch_ms_mean": t["attn_ms_mean"],
                 "launch_ms_min": t["attn_ms_min"], "flops_per_launch": flops}
     line = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -415,13 +458,17 @@ def main(argv=None) -> int:
         "roofline": roofline,
         "cpu_baseline": None,
     }
+    if step.tv is not None:
+        line["config"]["text_padding"] = {"kind": args.text_padding, "text_tokens": int(step.tv.shape[1]),
+                                          "valid_per_sample": step.tv.sum(axis=1).tolist()}
+        line["config"]["step"] = "token metadata + key validity + qk-rmsnorm/rope + padded attention"
     if args.multistep:
         ms = multistep(step, args.multistep, args.steps, args.warmup, t["step_ms"])
         log("multistep: %s" % json.dumps(ms))
         line["multistep"] = ms
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on host cores, ~%.0f s" % args.cpu_budget)
-        cb = cpu_baseline(w, step.drawn, args.cpu_budget)
+        cb = cpu_baseline(w, step.drawn, args.cpu_budget, step.tv)
         line["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
     print(json.dumps(line), flush=True)
     return 0

@@ -156,13 +156,19 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   // cache, outside the vector-memory counts the tile waits rely on; volatile
   // keeps it where it is written (before a tile barrier, whose wait then
   // covers its latency) instead of next to its use.
+  // The index goes in as a 32-bit byte offset, which the scalar load takes
+  // in a register as it is (no 64-bit address arithmetic per tile).
   using const_u64 = const volatile __attribute__((address_space(4))) uint64_t;
-  const_u64* kbits = nullptr;
-  if constexpr (PADDED) kbits = (const_u64*)(a.key_bits + (int64_t)b * a.kb_stride);
+  using const_u8 = const __attribute__((address_space(4))) char;
+  const_u8* kbits = nullptr;
+  if constexpr (PADDED) kbits = (const_u8*)(a.key_bits + (int64_t)b * a.kb_stride);
   auto tile_word = [&](int t) __attribute__((always_inline)) -> uint64_t {
-    if constexpr (PADDED) return kbits[t];
+    if constexpr (PADDED) return *(const_u64*)(kbits + ((uint32_t)t << 3));
     return ~0ull;
   };
+  // The first three tiles' words, read together while Q loads.
+  const int last_tile = (Sk - 1) / kTileN;
+  const uint64_t pw0 = tile_word(0), pw1 = tile_word(min(1, last_tile)), pw2 = tile_word(min(2, last_tile));
 
   // This lane's query row and its key bound.
   const int qrow = qtile * 32 * NW + wave * 32 + (lane & 31);
@@ -416,11 +422,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   f32x16 sA[2], sB[2];
   bf16x8 pop[2][2];
   float mx_cur = -INFINITY;
-  auto phase1 = [&](int t, const char* k_next, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2]) __attribute__((always_inline)) {
+  // t: the tile whose S is in s_cur; tn: the tile after it (t + 1, or without
+  // padding the next tile that holds a valid key); wn: tn's validity word.
+  auto phase1 = [&](int t, int tn, const char* k_next, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2])
+                    __attribute__((always_inline)) {
     const int k0 = t * kTileN;
     if (k0 >= wlim_max) return;  // wave-uniform: nothing allowed from here on
     update(mx_cur, s_cur);
-    const int k1 = k0 + kTileN;
+    const int k1 = PADDED ? tn * kTileN : k0 + kTileN;
     const bool has_next = k1 < wlim_max && k1 < Sk;
     softmax(s_cur, pop);
     if (has_next) {
@@ -439,17 +448,16 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
       }
     }
   };
-  // wn: validity word of tile t + 1 (loaded before the barrier that opens
-  // the phase, so the barrier wait covers its latency).
-  auto phase2 = [&](int t, const char* v_cur, f32x16 (&s_nxt)[2], uint64_t wn) __attribute__((always_inline)) {
+  auto phase2 = [&](int t, int tn, const char* v_cur, f32x16 (&s_nxt)[2], uint64_t wn)
+                    __attribute__((always_inline)) {
     const int k0 = t * kTileN;
     if (k0 >= wlim_max) return;
-    const int k1 = k0 + kTileN;
+    const int k1 = PADDED ? tn * kTileN : k0 + kTileN;
     const bool has_next = k1 < wlim_max && k1 < Sk;
     if (has_next) {
       if (k1 + kTileN > wlim_min || wn != ~0ull) {
         pv(v_cur, pop);
-        mask(t + 1, s_nxt, wn);
+        mask(PADDED ? tn : t + 1, s_nxt, wn);
         mx_cur = rowmax(s_nxt);
       } else {
         pv(v_cur, pop);
@@ -492,43 +500,100 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
     asm volatile("" ::: "memory");
   };
 
-  // Prologue: K(0), K(1), V(0); S(0) once they land; then K(2).
-  issue(0, sK0, true);
-  issue(1, sK1, true);
-  issue(0, sV0, false);
-  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-  qk(sK0, sA);
-  {
-    const uint64_t w0 = tile_word(0);
-    if (kTileN > wlim_min || w0 != ~0ull) mask(0, sA, w0);
-  }
-  mx_cur = rowmax(sA);
-  __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
-  __builtin_amdgcn_s_barrier();  // every wave is done with K(0)
-  asm volatile("" ::: "memory");
-  issue(2, sK0, true);
+  if constexpr (!PADDED) {
+    // Prologue: K(0), K(1), V(0); S(0) once they land; then K(2).
+    issue(0, sK0, true);
+    issue(1, sK1, true);
+    issue(0, sV0, false);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    qk(sK0, sA);
+    if (kTileN > wlim_min) mask(0, sA, ~0ull);
+    mx_cur = rowmax(sA);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+    __builtin_amdgcn_s_barrier();  // every wave is done with K(0)
+    asm volatile("" ::: "memory");
+    issue(2, sK0, true);
 
-  // Stages are named statically, two iterations per trip.  The validity word
-  // of a tile past the last one is never used; its index stays in the row.
-  const int last_tile = (Sk - 1) / kTileN;
-  for (int t = 0; t < n_tiles; t += 2) {
-    wait_tile();  // K(t+1) in sK1; sV1 (V(t-1)) read by every wave
-    issue(t + 1, sV1, false);
-    phase1(t, sK1, sA, sB);
-    const uint64_t w1 = tile_word(min(t + 1, last_tile));
-    wait_tile();  // V(t) in sV0; sK1 (K(t+1)) read by every wave
-    issue(t + 3, sK1, true);
-    phase2(t, sV0, sB, w1);
-    if (t + 1 >= n_tiles) break;
-    wait_tile();  // K(t+2) in sK0; sV0 (V(t)) read by every wave
-    issue(t + 2, sV0, false);
-    phase1(t + 1, sK0, sB, sA);
-    const uint64_t w2 = tile_word(min(t + 2, last_tile));
-    wait_tile();  // V(t+1) in sV1; sK0 (K(t+2)) read by every wave
-    issue(t + 4, sK0, true);
-    phase2(t + 1, sV1, sA, w2);
+    // Stages are named statically, two iterations per trip.
+    for (int t = 0; t < n_tiles; t += 2) {
+      wait_tile();  // K(t+1) in sK1; sV1 (V(t-1)) read by every wave
+      issue(t + 1, sV1, false);
+      phase1(t, t + 1, sK1, sA, sB);
+      wait_tile();  // V(t) in sV0; sK1 (K(t+1)) read by every wave
+      issue(t + 3, sK1, true);
+      phase2(t, t + 1, sV0, sB, ~0ull);
+      if (t + 1 >= n_tiles) break;
+      wait_tile();  // K(t+2) in sK0; sV0 (V(t)) read by every wave
+      issue(t + 2, sV0, false);
+      phase1(t + 1, t + 2, sK0, sB, sA);
+      wait_tile();  // V(t+1) in sV1; sK0 (K(t+2)) read by every wave
+      issue(t + 4, sK0, true);
+      phase2(t + 1, t + 2, sV1, sA, ~0ull);
+    }
+  } else {
+    // Padded keys: the same schedule over the tiles that hold a valid key.
+    // Iteration i runs tile T(i); tiles whose validity word is 0 are never
+    // loaded or computed (they would add probability 0 to every row).  T(i+3)
+    // is needed at the middle of iteration i: its first candidate's word is
+    // read before the barrier there (whose wait covers the load) and only a
+    // run of empty tiles costs further, serial reads.  Indices at or past
+    // n_tiles are dead tiles (zero loads, phases return at once).
+    auto skip_empty = [&](int x, uint64_t& w) __attribute__((always_inline)) {
+      if (w == 0) {  // rare: a run of empty tiles (or a dead index)
+        while (x < n_tiles && w == 0) {
+          ++x;
+          w = tile_word(min(x, last_tile));
+        }
+      }
+      return x;
+    };
+    uint64_t w0 = pw0;
+    const int t0 = skip_empty(0, w0);
+    uint64_t w1 = t0 == 0 ? pw1 : tile_word(min(t0 + 1, last_tile));
+    int ta = t0, tb = skip_empty(t0 + 1, w1);  // T(i), T(i+1)
+    uint64_t w2 = tb == 1 ? pw2 : tile_word(min(tb + 1, last_tile));
+    int tc = skip_empty(tb + 1, w2);  // T(i+2)
+    uint64_t wb = w1, wc = w2;        // words of T(i+1), T(i+2)
+
+    issue(t0, sK0, true);
+    issue(tb, sK1, true);
+    issue(t0, sV0, false);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    qk(sK0, sA);
+    if ((t0 + 1) * kTileN > wlim_min || w0 != ~0ull) mask(t0, sA, w0);
+    mx_cur = rowmax(sA);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+    __builtin_amdgcn_s_barrier();  // every wave is done with K(T(0))
+    asm volatile("" ::: "memory");
+    issue(tc, sK0, true);
+
+    while (ta < n_tiles) {
+      wait_tile();  // K(T(i+1)) in sK1
+      issue(tb, sV1, false);
+      phase1(ta, tb, sK1, sA, sB);
+      uint64_t wd = tile_word(min(tc + 1, last_tile));
+      wait_tile();  // V(T(i)) in sV0
+      int td = skip_empty(tc + 1, wd);  // T(i+3)
+      issue(td, sK1, true);
+      phase2(ta, tb, sV0, sB, wb);
+      ta = tb, tb = tc, tc = td;
+      wb = wc, wc = wd;
+      if (ta >= n_tiles) break;
+      wait_tile();  // K(T(i+2)) in sK0
+      issue(tb, sV0, false);
+      phase1(ta, tb, sK0, sB, sA);
+      wd = tile_word(min(tc + 1, last_tile));
+      wait_tile();  // V(T(i+1)) in sV1
+      td = skip_empty(tc + 1, wd);
+      issue(td, sK0, true);
+      phase2(ta, tb, sV1, sA, wb);
+      ta = tb, tb = tc, tc = td;
+      wb = wc, wc = wd;
+    }
   }
   // Tiles past the last one were issued too: drain before the work-group's
   // LDS can be handed to another.

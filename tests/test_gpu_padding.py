@@ -209,6 +209,33 @@ def test_padded_attention_all_rows(dit, case, prescaled):
         assert np.isneginf(rl).any()  # the case does exercise rows with no valid key
 
 
+@pytest.mark.parametrize("mode", ["block_causal", "full"])
+def test_runs_of_empty_tiles(dit, mode):
+    """Padded runs that empty whole 64-key tiles (the kernel never visits
+    those tiles): a run at key 0, runs of odd and even tile counts, a run
+    reaching the end of a text segment; sample 1 unpadded in the same launch."""
+    layout = (("T", 400), ("I", 1, 8, 16), ("T", 300), ("I", 1, 10, 12))
+    w = wl.small_workload("r", 2, 4, 2, 128, layout, (128,), seed=31, mask_mode=mode)
+    d = wl.draw(w)
+    mask, shapes = wl.sequence_inputs(w)
+    md = ometa.build_token_metadata(mask, shapes)
+    m = dit.build_token_metadata(torch.from_numpy(mask).cuda(), shapes)
+    tv = np.ones((2, 700), dtype=np.uint8)
+    for a, b in ((0, 150), (200, 330), (390, 520), (600, 700)):  # text ordinals
+        tv[0, a:b] = 0
+    valid = okp.joint_key_valid(mask, tv)
+    kv = _build(dit, mask, tv)
+    q, k, v = (to_device(d.bits[n], "bf16") for n in ("q", "k", "v"))
+    o, lse = dit.forward(q, k, v, mode, m, return_lse=True, key_valid=kv)
+    o1, lse1 = dit.forward(q[1:], k[1:], v[1:], mode, m, return_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = oatt.attention(d.vals["q"], d.vals["k"], d.vals["v"], md["image_ids"], mode, key_valid=valid)
+    assert_parity(to_host(o), ro, "bf16", "O")
+    _check_lse(lse.cpu().double().numpy(), rl, "bf16")
+    # the all-valid sample matches the unpadded kernel bit for bit
+    assert torch.equal(o[1:], o1) and torch.equal(lse[1:], lse1)
+
+
 def test_all_valid_bits_match_unpadded_bitwise(dit):
     """Every bit set: the padded kernels give the unpadded results bit for bit
     (bf16 and f32, plain and cached)."""
