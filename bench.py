@@ -353,7 +353,7 @@ def main(argv=None) -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=list(wl.WORKLOADS))
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=list(wl.WORKLOADS) + list(wl.VARIANTS))
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the host oracle timing")
     ap.add_argument("--multistep", type=int, default=0, metavar="N",
                     help="also time N denoising steps: one full step, then N-1 steps that recompute only the "
@@ -392,7 +392,7 @@ def main(argv=None) -> int:
         log("copied %d bytes five times" % n)
         return 0
 
-    w = wl.WORKLOADS[args.workload]
+    w = wl.get(args.workload)
     if args.shard_heads > 1:
         K = args.shard_heads
         if w.heads % K or w.kv_heads % K:

@@ -334,3 +334,73 @@ def test_padded_pipeline_workloads(dit, name):
     _check_lse(lse[:, :, idx].cpu().double().numpy(), rl, w.dtype)
     _say("  %s valid text %s rows=%d max=%.3g mean=%.3g" % (name, tv.sum(axis=1).tolist(), rows.size,
                                                             stats["max"], stats["mean"]))
+
+
+# --------------------------------------------------------------------------- image-query joint attention
+@pytest.mark.parametrize("kind", ["right", "random"])
+@pytest.mark.parametrize("heads", [(4, 1), (4, 4)], ids=["gqa4", "mha"])
+def test_image_query_attention_key_order(dit, kind, heads):
+    """NucleusMoE-style attention: image queries over the image keys and the
+    text keys, every pair allowed, padded text keys left out.  The GPU takes
+    the text as the cached prefix (keys [text; image]); the oracle gets the
+    keys in the article's order [image; text].  Under the full mask the key
+    order is not part of the result."""
+    H, Hk = heads
+    n_text = 150
+    layout = (("T", n_text), ("I", 1, 10, 12))
+    w = wl.small_workload("n", 2, H, Hk, 128, layout, (16, 56, 56), seed=H + Hk, prefix_len=n_text,
+                          mask_mode="full")
+    d = wl.draw(w)
+    mask, shapes = wl.sequence_inputs(w)
+    tv = wl.text_mask(w, 17, kind)
+    kv = _build(dit, mask, tv)
+    q, k, v = (to_device(d.bits[n], "bf16") for n in ("q", "k", "v"))
+    kc, vc = to_device(d.bits["k_cache"], "bf16"), to_device(d.bits["v_cache"], "bf16")
+    o, lse = dit.forward_cached(q, kc, vc, k, v, "full", return_lse=True, key_valid=kv)
+    torch.cuda.synchronize()
+    n_img = w.n_new
+    k_img_txt = np.concatenate([d.vals["k"], d.vals["k_cache"]], axis=1)
+    v_img_txt = np.concatenate([d.vals["v"], d.vals["v_cache"]], axis=1)
+    valid = np.concatenate([np.ones((2, n_img), bool), tv.astype(bool)], axis=1)
+    ro, rl = oatt.attention(d.vals["q"], k_img_txt, v_img_txt, np.zeros(n_img + n_text, np.int32), "full",
+                            key_valid=valid)
+    assert_parity(to_host(o), ro, "bf16", "O")
+    _check_lse(lse.cpu().double().numpy(), rl, "bf16")
+
+
+def test_image_query_workload_sampled(dit):
+    """The NucleusMoE image-query variant at full size (B 2, 16 heads x 128,
+    1024 cached text keys of which a right-padded prefix is valid, 4096 image
+    queries): metadata + key validity -> norm+rope (prescaled Q) -> padded
+    cached attention, sampled rows against the oracle."""
+    w = wl.get("nucleus_image_query_t1024_i64x64")
+    _say("image-query variant %s" % w.name)
+    d = wl.draw(w)
+    mask, shapes = wl.sequence_inputs(w)
+    md = ometa.build_token_metadata(mask, shapes, w.pos_mode)
+    m = dit.build_token_metadata(torch.from_numpy(mask).cuda(), shapes, w.pos_mode)
+    m.check()
+    tv = wl.text_mask(w, 2024, "right")
+    valid = okp.joint_key_valid(mask, tv)
+    kv = _build(dit, mask, tv)
+    P = w.prefix_len
+    q, k, v = (to_device(d.bits[n], w.dtype) for n in ("q", "k", "v"))
+    wq, wk = to_device(d.bits["wq"], w.dtype), to_device(d.bits["wk"], w.dtype)
+    kc, vc = to_device(d.bits["k_cache"], w.dtype), to_device(d.bits["v_cache"], w.dtype)
+    qp, kp = dit.qknorm_rope(q, k, m.pos_ids[P:], w.axes, w.eps, wq, wk,
+                             q_scale=dit.prescaled_q_factor(w.head_dim))
+    o, lse = dit.forward_cached(qp, kc, vc, kp, v, "full", m, softmax_scale=dit.LN2, return_lse=True,
+                                key_valid=kv)
+    torch.cuda.synchronize()
+    rows = sample_rows(w)
+    pos = md["pos_ids"][P:]
+    rq = oqr.qknorm_rope(d.vals["q"][:, rows], d.vals["wq"], w.eps, pos[rows], w.axes)
+    rk = oqr.qknorm_rope(d.vals["k"], d.vals["wk"], w.eps, pos, w.axes)
+    k_all = np.concatenate([d.vals["k_cache"], rk], axis=1)
+    v_all = np.concatenate([d.vals["v_cache"], d.vals["v"]], axis=1)
+    ro, rl = oatt.attention(rq, k_all, v_all, md["image_ids"], "full", q_offset=P, key_valid=valid)
+    idx = torch.from_numpy(rows).cuda()
+    stats = assert_parity(to_host(o[:, idx]), ro, w.dtype, "O")
+    _check_lse(lse[:, :, idx].cpu().double().numpy(), rl, w.dtype)
+    _say("  valid text %s rows=%d max=%.3g mean=%.3g" % (tv.sum(axis=1).tolist(), rows.size, stats["max"],
+                                                        stats["mean"]))

@@ -25,7 +25,7 @@ from typing import Dict, List, Sequence, Tuple
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "get", "sequence_inputs", "draw", "bf16_round_bits",
+__all__ = ["Workload", "WORKLOADS", "VARIANTS", "get", "sequence_inputs", "draw", "bf16_round_bits",
            "bf16_bits_to_f64", "small_workload", "n_text_tokens", "text_mask"]
 
 
@@ -90,10 +90,25 @@ WORKLOADS: Dict[str, Workload] = {w.name: w for w in [
 # The order in which the five configurations are usually listed.
 ORDER: List[str] = list(WORKLOADS)
 
+# Variants beyond the five configurations.
+#   NucleusMoE image-query attention (NucleusMoE-Image article, section 6 for
+#   16 heads x 128 and axes (16, 56, 56); section 6.3 for image queries only,
+#   over the image keys and the cached text keys, every pair allowed).  The
+#   text is the cached prefix (its K/V do not change across steps) and the
+#   64x64 image tokens are the queries; a CFG pair.  The article gives no KV
+#   head count: 16, no grouping.
+VARIANTS: Dict[str, Workload] = {w.name: w for w in [
+    Workload("nucleus_image_query_t1024_i64x64", 2, 16, 16, 128, (("T", 1024), ("I", 1, 64, 64)), (16, 56, 56),
+             "centered_fhw", "full", 1e-6, "bf16", False, 5, prefix_len=1024,
+             description="4096 image queries over 1024 cached text + 4096 image keys, full mask"),
+]}
+
 
 def get(name_or_index) -> Workload:
     if isinstance(name_or_index, int):
         return WORKLOADS[ORDER[name_or_index]]
+    if name_or_index in VARIANTS:
+        return VARIANTS[name_or_index]
     return WORKLOADS[name_or_index]
 
 
