@@ -18,6 +18,11 @@ float64 NumPy, slow and plain:
   K, then rotary embedding over the (frame, height, width) axes or the
   Lumina 2D split (NucleusMoE-Image pipeline article, section 6.3; Lumina-Next
   DiT article, configuration table and section 4).
+* ``qknorm_rope.layer_norm_across_heads``, the ``linear_factor`` /
+  ``ntk_factor`` of ``rope`` and ``qknorm_rope.time_aware_rope_factors`` --
+  the Lumina-Next variants: LayerNorm over all heads' channels, and the
+  rotary table rescaled per denoising step (Lumina-Next DiT article,
+  sections 3 and 4).
 * ``attention.attention`` -- softmax attention under the full mask or the
   block-causal rule "q_idx >= kv_idx or same image block", with GQA and an
   optional cached K/V prefix (QwenImage21Transformer2DModel API page, the

@@ -181,6 +181,76 @@ def pin_rope_relative():
         assert abs(d0 - d1) < 1e-9 * (1 + abs(d0))
 
 
+# --------------------------------------------------------------------------- Lumina-Next variants
+def pin_layernorm_across_heads():
+    """LayerNorm over all heads' channels of a token (Lumina-Next DiT article,
+    section 3): = torch.nn.functional.layer_norm (float64) on the flattened
+    heads x head_dim channels with the same weight and bias; closed forms of
+    the output's mean and variance; invariant to a shift of the token; the
+    heads' relative scale survives (a per-head norm would erase it)."""
+    x = _rand((2, 5, 4, 18), 31) * 3.0 + 0.7
+    H, D = 4, 18
+    w = 1.0 + 0.1 * _rand((H * D,), 32)
+    b = 0.05 * _rand((H * D,), 33)
+    for eps in (1e-5, 0.5):
+        y = qr.layer_norm_across_heads(x, w, b, eps)
+        ref = torch.nn.functional.layer_norm(torch.from_numpy(x.reshape(2, 5, H * D)), (H * D,),
+                                             torch.from_numpy(w), torch.from_numpy(b), eps)
+        assert np.allclose(y.reshape(2, 5, H * D), ref.numpy(), rtol=1e-12, atol=1e-13)
+    # unit affine: mean 0 and variance v / (v + eps) over the token's channels
+    eps = 0.5
+    y = qr.layer_norm_across_heads(x, None, None, eps).reshape(2, 5, H * D)
+    v = x.reshape(2, 5, H * D).var(axis=-1)
+    assert np.allclose(y.mean(axis=-1), 0.0, atol=1e-13)
+    assert np.allclose(y.var(axis=-1), v / (v + eps), rtol=1e-12)
+    # a constant added to every channel of a token changes nothing
+    assert np.allclose(qr.layer_norm_across_heads(x + 5.0, w, b, 1e-5), qr.layer_norm_across_heads(x, w, b, 1e-5),
+                       rtol=1e-9, atol=1e-10)
+    # head 0 ten times larger than head 1 stays ten times larger (eps = 0, zero-mean heads)
+    z = _rand((1, 1, 2, 8), 34)
+    z -= z.mean(axis=-1, keepdims=True)
+    z[0, 0, 1] = z[0, 0, 0] / 10.0
+    yz = qr.layer_norm_across_heads(z, None, None, 0.0)
+    assert abs(np.linalg.norm(yz[0, 0, 0]) / np.linalg.norm(yz[0, 0, 1]) - 10.0) < 1e-12
+
+
+def pin_scaled_rope():
+    """Rotary factors (Lumina-Next DiT article, section 4): with the linear
+    factor L a position L * p turns pair 0 of every axis by exactly p rad, as a
+    position p does unscaled; the NTK factor N leaves pair 0 (frequency 1)
+    alone and moves the ladder to (theta * N)^(-2j/d): theta 100, N 4, d 4,
+    j 1 -> 1/20, so position 20 turns that pair by exactly 1 rad.  Rotations
+    stay rotations and factors 1 change nothing."""
+    x = _rand((1, 3, 2, 8), 35)
+    pos = np.array([[0, 7, 0], [0, 0, 11], [0, 5, 9]])
+    axes = (4, 4)
+    pos2 = pos[:, 1:]
+    for L in (2.0, 3.0):
+        assert np.allclose(qr.rope(x, L * pos2, axes, linear_factor=L), qr.rope(x, pos2, axes), rtol=1e-13,
+                           atol=1e-14)
+    e = np.zeros((1, 1, 1, 8))
+    e[..., 2] = 1.0  # axis 0, pair 1
+    y = qr.rope(e, np.array([[20, 0]]), axes, theta=100.0, ntk_factor=4.0)[0, 0, 0]
+    assert abs(y[2] - math.cos(1.0)) < 1e-14 and abs(y[3] - math.sin(1.0)) < 1e-14
+    e0 = np.zeros((1, 1, 1, 8))
+    e0[..., 4] = 1.0  # axis 1, pair 0
+    y0 = qr.rope(e0, np.array([[0, 3]]), axes, ntk_factor=7.0)[0, 0, 0]
+    assert abs(y0[4] - math.cos(3.0)) < 1e-15 and abs(y0[5] - math.sin(3.0)) < 1e-15
+    y = qr.rope(x, pos2, axes, linear_factor=1.7, ntk_factor=3.1)
+    assert np.allclose(np.hypot(y[..., 0::2], y[..., 1::2]), np.hypot(x[..., 0::2], x[..., 1::2]), rtol=1e-12)
+    assert np.array_equal(qr.rope(x, pos2, axes, linear_factor=1.0, ntk_factor=1.0), qr.rope(x, pos2, axes))
+
+
+def pin_time_aware_factors():
+    """Lumina-Next DiT article, section 4: one factor carries scaling_factor,
+    the other is 1, switched at scaling_watershed (reading: steps before the
+    watershed take the linear factor)."""
+    assert qr.time_aware_rope_factors(0.1, 0.3, 2.0) == (2.0, 1.0)
+    assert qr.time_aware_rope_factors(0.3, 0.3, 2.0) == (1.0, 2.0)
+    assert qr.time_aware_rope_factors(0.9, 0.3, 2.0) == (1.0, 2.0)
+    assert qr.time_aware_rope_factors(0.5, 0.3, 1.0) == (1.0, 1.0)
+
+
 # --------------------------------------------------------------------------- attention
 def pin_full_is_sdpa():
     """One image block and no text: the full mask and the block-causal mask both
@@ -413,4 +483,5 @@ ALL_PINS = [pin_metadata_goldens, pin_kv_limit_is_predicate_prefix, pin_metadata
             pin_full_is_sdpa, pin_text_only_is_causal, pin_gqa_is_repeat_interleave,
             pin_singlepass_equals_multipass, pin_adjacent_blocks_stay_separate, pin_cached_equals_full,
             pin_bruteforce_tiny, pin_lse_definition, pin_key_padding_fixtures, pin_key_padding_is_masked_sdpa,
-            pin_key_padding_is_compaction, pin_key_padding_bruteforce_and_empty_rows]
+            pin_key_padding_is_compaction, pin_key_padding_bruteforce_and_empty_rows, pin_layernorm_across_heads,
+            pin_scaled_rope, pin_time_aware_factors]

@@ -43,10 +43,11 @@ def _rms_eps_outside(x, weight, eps):
     return x / (np.sqrt(np.mean(x * x, axis=-1, keepdims=True)) + eps) * weight
 
 
-def _rope_rotate_half(x, pos, axes, theta=10000.0):
+def _rope_rotate_half(x, pos, axes, theta=10000.0, linear_factor=1.0, ntk_factor=1.0):
     x = np.asarray(x, dtype=np.float64)
     y = x.copy()
-    pos = np.asarray(pos, dtype=np.float64)
+    pos = np.asarray(pos, dtype=np.float64) / linear_factor
+    theta = theta * ntk_factor
     off = 0
     for a, d_a in enumerate(axes):
         half = d_a // 2
@@ -60,12 +61,13 @@ def _rope_rotate_half(x, pos, axes, theta=10000.0):
     return y
 
 
-def _rope_shared_ladder(x, pos, axes, theta=10000.0):
+def _rope_shared_ladder(x, pos, axes, theta=10000.0, linear_factor=1.0, ntk_factor=1.0):
     """Mistake: one frequency ladder over the whole head instead of per axis."""
     x = np.asarray(x, dtype=np.float64)
     y = x.copy()
     D = x.shape[-1]
-    pos = np.asarray(pos, dtype=np.float64)
+    pos = np.asarray(pos, dtype=np.float64) / linear_factor
+    theta = theta * ntk_factor
     off = 0
     for a, d_a in enumerate(axes):
         for j in range(d_a // 2):
@@ -78,8 +80,48 @@ def _rope_shared_ladder(x, pos, axes, theta=10000.0):
     return y
 
 
-def _rope_sign_flip(x, pos, axes, theta=10000.0):
-    return qr_rope_orig(x, -np.asarray(pos), axes, theta)
+def _rope_sign_flip(x, pos, axes, theta=10000.0, linear_factor=1.0, ntk_factor=1.0):
+    return qr_rope_orig(x, -np.asarray(pos), axes, theta, linear_factor, ntk_factor)
+
+
+def _rope_ntk_as_interpolation(x, pos, axes, theta=10000.0, linear_factor=1.0, ntk_factor=1.0):
+    # Mistake: the NTK factor divides the positions like the linear one.
+    return qr_rope_orig(x, pos, axes, theta, linear_factor * ntk_factor, 1.0)
+
+
+def _rope_linear_multiplies(x, pos, axes, theta=10000.0, linear_factor=1.0, ntk_factor=1.0):
+    # Mistake: the linear factor multiplies the positions.
+    return qr_rope_orig(x, pos, axes, theta, 1.0 / linear_factor, ntk_factor)
+
+
+def _ln_per_head(x, weight=None, bias=None, eps=1e-5):
+    # Mistake: each head normalised on its own.
+    x = np.asarray(x, dtype=np.float64)
+    cen = x - x.mean(axis=-1, keepdims=True)
+    y = cen / np.sqrt((cen * cen).mean(axis=-1, keepdims=True) + eps)
+    y = y.reshape(x.shape[:-2] + (-1,))
+    if weight is not None:
+        y = y * weight
+    if bias is not None:
+        y = y + bias
+    return y.reshape(x.shape)
+
+
+def _ln_no_centering(x, weight=None, bias=None, eps=1e-5):
+    # Mistake: RMS over the heads' channels (mean not removed).
+    x = np.asarray(x, dtype=np.float64)
+    flat = x.reshape(x.shape[:-2] + (-1,))
+    y = flat / np.sqrt((flat * flat).mean(axis=-1, keepdims=True) + eps)
+    if weight is not None:
+        y = y * weight
+    if bias is not None:
+        y = y + bias
+    return y.reshape(x.shape)
+
+
+def _time_aware_swapped(t, watershed, scaling_factor):
+    # Mistake: the branches swapped.
+    return (1.0, float(scaling_factor)) if t < watershed else (float(scaling_factor), 1.0)
 
 
 qr_rope_orig = qr.rope
@@ -190,6 +232,11 @@ MUTATIONS = [
     ("metadata_positions_uncentred", meta, "build_token_metadata", _metadata_uncentred),
     ("padding_masks_queries_not_keys", att, "attention", _attention_padding_masks_queries),
     ("padding_flag_by_position", kp, "joint_key_valid", _key_valid_by_position),
+    ("rope_ntk_as_interpolation", qr, "rope", _rope_ntk_as_interpolation),
+    ("rope_linear_multiplies_positions", qr, "rope", _rope_linear_multiplies),
+    ("layernorm_per_head", qr, "layer_norm_across_heads", _ln_per_head),
+    ("layernorm_without_centering", qr, "layer_norm_across_heads", _ln_no_centering),
+    ("time_aware_branches_swapped", qr, "time_aware_rope_factors", _time_aware_swapped),
 ]
 
 
