@@ -102,6 +102,11 @@ class Step:
             return torch.from_numpy(bits).to(device)
         self.q, self.k, self.v = dev("q"), dev("k"), dev("v")
         self.wq, self.wk = dev("wq"), dev("wk")
+        across = w.qk_norm == "layer_across_heads"
+        self.bq, self.bk = (dev("bq"), dev("bk")) if across else (None, None)
+        # Norm and rotary options of the workload, as qknorm_rope keywords.
+        self.norm_kw = dict(norm=w.qk_norm, q_bias=self.bq, k_bias=self.bk, rope_linear_factor=w.rope_linear,
+                            rope_ntk_factor=w.rope_ntk)
         self.kc = dev("k_cache") if w.prefix_len else None
         self.vc = dev("v_cache") if w.prefix_len else None
         mask, self.shapes = wl.sequence_inputs(w)
@@ -130,7 +135,8 @@ class Step:
         # so the attention exponentiates its MFMA output directly.
         P = self.w.prefix_len
         self.dit.qknorm_rope(self.q, self.k, self.meta.pos_ids[P:], self.w.axes, self.w.eps, self.wq, self.wk,
-                             q_out=self.qp, k_out=self.kp, q_scale=self.dit.prescaled_q_factor(self.w.head_dim))
+                             q_out=self.qp, k_out=self.kp, q_scale=self.dit.prescaled_q_factor(self.w.head_dim),
+                             **self.norm_kw)
 
     def attention(self):
         if self.w.prefix_len:
@@ -187,7 +193,7 @@ def time_norm_cold(step: Step, reps: int = 30, copies: int = 3):
 
     def launch(i):
         dit.qknorm_rope(qs[i % copies], ks[i % copies], step.meta.pos_ids[P:], w.axes, w.eps, step.wq, step.wk,
-                        q_out=step.qp, k_out=step.kp, q_scale=scale)
+                        q_out=step.qp, k_out=step.kp, q_scale=scale, **step.norm_kw)
     for i in range(copies):
         launch(i)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
@@ -226,7 +232,7 @@ def multistep(step: Step, n_steps: int, reps: int, warmup: int, full_ms: float):
 
     def cached():
         dit.qknorm_rope(q_new, k_new, step.meta.pos_ids[P:], w.axes, w.eps, step.wq, step.wk,
-                        q_out=qp_new, k_out=kp_new, q_scale=scale)
+                        q_out=qp_new, k_out=kp_new, q_scale=scale, **step.norm_kw)
         dit.forward_cached(qp_new, k_cache, v_cache, kp_new, v_new, w.mask_mode, step.meta,
                            softmax_scale=dit.LN2, out=o_new, key_valid=step.kv)
     step.run()
@@ -266,7 +272,8 @@ def cpu_baseline(w: wl.Workload, drawn: wl.Drawn, budget_s: float = 12.0, text_v
     P = w.prefix_len
     pos = md["pos_ids"][P:]
     t0 = time.perf_counter()
-    kp = oqr.qknorm_rope(drawn.vals["k"], drawn.vals["wk"], w.eps, pos, w.axes)
+    nkw = dict(norm=w.qk_norm, linear_factor=w.rope_linear, ntk_factor=w.rope_ntk)
+    kp = oqr.qknorm_rope(drawn.vals["k"], drawn.vals["wk"], w.eps, pos, w.axes, bias=drawn.vals.get("bk"), **nkw)
     k_all = np.concatenate([drawn.vals["k_cache"], kp], axis=1) if P else kp
     v_all = np.concatenate([drawn.vals["v_cache"], drawn.vals["v"]], axis=1) if P else drawn.vals["v"]
     valid = okp.joint_key_valid(mask, text_valid) if text_valid is not None else None
@@ -277,7 +284,8 @@ def cpu_baseline(w: wl.Workload, drawn: wl.Drawn, budget_s: float = 12.0, text_v
     chunk = 64
     while time.perf_counter() - t0 < budget_s:
         rows = np.sort(rng.choice(w.n_new, size=chunk, replace=False))
-        qp = oqr.qknorm_rope(drawn.vals["q"][:, rows], drawn.vals["wq"], w.eps, pos[rows], w.axes)
+        qp = oqr.qknorm_rope(drawn.vals["q"][:, rows], drawn.vals["wq"], w.eps, pos[rows], w.axes,
+                             bias=drawn.vals.get("bq"), **nkw)
         for j, r in enumerate(rows):
             oatt.attention(qp[:, j:j + 1], k_all, v_all, md["image_ids"], w.mask_mode, q_offset=P + int(r),
                            key_valid=valid)
@@ -433,7 +441,8 @@ def main(argv=None) -> int:
 
     roofline = {"bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": attn_tflops / PEAK_BF16_TFLOPS, "traffic": measured_traffic(w),
-                "kernel": "attn_fwd_bf16_kernel<128,4%s>" % (",padded" if step.kv is not None else ""), "launch_ms_mean": t["attn_ms_mean"],
+                "kernel": "attn_fwd_bf16_kernel<%d,4%s>" % ((w.head_dim + 31) // 32 * 32,
+                                                            ",padded" if step.kv is not None else ""), "launch_ms_mean": t["attn_ms_mean"],
                 "launch_ms_min": t["attn_ms_min"], "flops_per_launch": flops}
     line = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -441,7 +450,10 @@ def main(argv=None) -> int:
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "kv_heads": w.kv_heads,
                    "head_dim": w.head_dim, "seq_len": w.seq_len, "queries": w.n_new, "mask": w.mask_mode,
-                   "rope_axes": list(w.axes), "step": "token metadata + qk-rmsnorm/rope + attention"},
+                   "rope_axes": list(w.axes), "qk_norm": w.qk_norm, "rope_linear_factor": w.rope_linear,
+                   "rope_ntk_factor": w.rope_ntk,
+                   "step": "token metadata + qk-%s/rope + attention" % (
+                       "rmsnorm" if w.qk_norm == "rms_per_head" else "layernorm-across-heads")},
         "pct_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
         "attention_only": {"tflops": attn_tflops, "pct_bf16_peak": 100.0 * attn_tflops / PEAK_BF16_TFLOPS,
                            "ms_mean": t["attn_ms_mean"], "ms_median": t["attn_ms_median"],

@@ -18,14 +18,24 @@ MASK_FULL, MASK_BLOCK_CAUSAL = 0, 1
 POS_CENTERED_FHW, POS_GRID_HW = 0, 1
 MAX_IMAGES = 64
 
+NORM_RMS_PER_HEAD, NORM_LAYER_ACROSS_HEADS = 0, 1
+
 EXPORTED = ("dit_attn_build_token_metadata", "dit_attn_build_key_valid", "dit_attn_qknorm_rope",
-            "dit_attn_forward", "dit_attn_forward_cached", "dit_attn_forward_padded",
-            "dit_attn_forward_cached_padded", "dit_attn_status_string")
+            "dit_attn_qknorm_rope_ex", "dit_attn_time_aware_rope_factors", "dit_attn_forward",
+            "dit_attn_forward_cached", "dit_attn_forward_padded", "dit_attn_forward_cached_padded",
+            "dit_attn_status_string")
 
 
 class TokenMetaStruct(ctypes.Structure):
     _fields_ = [("image_ids", ctypes.c_void_p), ("target_mask", ctypes.c_void_p),
                 ("pos_ids", ctypes.c_void_p), ("kv_limit", ctypes.c_void_p), ("seq_len", ctypes.c_int32)]
+
+
+class NormRopeParams(ctypes.Structure):
+    _fields_ = [("norm", ctypes.c_int32), ("q_weight", ctypes.c_void_p), ("k_weight", ctypes.c_void_p),
+                ("q_bias", ctypes.c_void_p), ("k_bias", ctypes.c_void_p), ("eps", ctypes.c_float),
+                ("rope_theta", ctypes.c_float), ("rope_linear_factor", ctypes.c_float),
+                ("rope_ntk_factor", ctypes.c_float), ("q_scale", ctypes.c_float)]
 
 
 Strides3 = ctypes.c_int64 * 3
@@ -43,6 +53,10 @@ def _load() -> ctypes.CDLL:
     lib.dit_attn_qknorm_rope.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                          Strides3, Strides3, Strides3, Strides3, vp, i32,
                                          ctypes.POINTER(i32), f32, f32, f32, i32, vp]
+    lib.dit_attn_qknorm_rope_ex.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, Strides3, Strides3, Strides3,
+                                            Strides3, vp, i32, ctypes.POINTER(i32), ctypes.POINTER(NormRopeParams),
+                                            i32, vp]
+    lib.dit_attn_time_aware_rope_factors.argtypes = [f32, f32, f32, ctypes.POINTER(f32), ctypes.POINTER(f32)]
     lib.dit_attn_forward.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, Strides3 * 4, i32,
                                      ctypes.POINTER(TokenMetaStruct), f32, i32, vp]
     lib.dit_attn_forward_cached.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,

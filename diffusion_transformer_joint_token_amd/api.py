@@ -17,9 +17,11 @@ from . import _lib
 from ._lib import DitAttnError, check, lib
 
 __all__ = ["TokenMeta", "KeyValid", "DitAttnError", "LN2", "LOG2E", "prescaled_q_factor",
-           "dit_attn_build_token_metadata", "dit_attn_build_key_valid", "dit_attn_qknorm_rope", "dit_attn_forward",
+           "dit_attn_build_token_metadata", "dit_attn_build_key_valid", "dit_attn_qknorm_rope",
+           "dit_attn_qknorm_rope_ex", "dit_attn_time_aware_rope_factors", "dit_attn_forward",
            "dit_attn_forward_cached", "dit_attn_forward_padded", "dit_attn_forward_cached_padded",
-           "build_token_metadata", "build_key_valid", "qknorm_rope", "forward", "forward_cached"]
+           "build_token_metadata", "build_key_valid", "qknorm_rope", "time_aware_rope_factors", "forward",
+           "forward_cached"]
 
 _POS = {"centered_fhw": _lib.POS_CENTERED_FHW, "grid_hw": _lib.POS_GRID_HW}
 
@@ -156,12 +158,27 @@ def _key_bits(key_valid) -> Tuple[int, int]:
     return bits.data_ptr(), bits.stride(0) if bits.shape[0] > 1 else bits.shape[1]
 
 
+_NORM = {"rms_per_head": _lib.NORM_RMS_PER_HEAD, "layer_across_heads": _lib.NORM_LAYER_ACROSS_HEADS}
+
+
+def dit_attn_time_aware_rope_factors(t: float, watershed: float, scaling_factor: float) -> Tuple[float, float]:
+    """(linear_factor, ntk_factor) of a denoising step at reversed timestep t."""
+    lin, ntk = ctypes.c_float(), ctypes.c_float()
+    check(lib.dit_attn_time_aware_rope_factors(float(t), float(watershed), float(scaling_factor), ctypes.byref(lin),
+                                               ctypes.byref(ntk)), "dit_attn_time_aware_rope_factors")
+    return lin.value, ntk.value
+
+
 def dit_attn_qknorm_rope(q: torch.Tensor, k: torch.Tensor, pos_ids: torch.Tensor, axes_dims: Sequence[int],
                          eps: float, q_weight: Optional[torch.Tensor] = None,
                          k_weight: Optional[torch.Tensor] = None, rope_theta: float = 10000.0,
                          q_out: Optional[torch.Tensor] = None, k_out: Optional[torch.Tensor] = None,
                          inplace: bool = False, q_scale: float = 1.0,
-                         stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+                         stream=None, norm: str = "rms_per_head", q_bias: Optional[torch.Tensor] = None,
+                         k_bias: Optional[torch.Tensor] = None, rope_linear_factor: float = 1.0,
+                         rope_ntk_factor: float = 1.0) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Q/K norm + rotary embedding.  The defaults call dit_attn_qknorm_rope;
+    another norm, a bias or a rotary factor calls dit_attn_qknorm_rope_ex."""
     if inplace:
         q_out, k_out = q, k
     if q_out is None:
@@ -174,19 +191,61 @@ def dit_attn_qknorm_rope(q: torch.Tensor, k: torch.Tensor, pos_ids: torch.Tensor
         raise DitAttnError(_lib.ERR_SHAPE, "q/k/out shapes disagree")
     if pos_ids.dtype != torch.int32 or not pos_ids.is_contiguous() or pos_ids.numel() < 3 * S:
         raise DitAttnError(_lib.ERR_SHAPE, "pos_ids must be contiguous int32 [S, 3]")
-    for w in (q_weight, k_weight):
-        if w is not None and (w.dtype != q.dtype or w.numel() != D or not w.is_contiguous()):
-            raise DitAttnError(_lib.ERR_SHAPE, "norm weights must be contiguous [head_dim] in the input dtype")
+    if norm not in _NORM:
+        raise DitAttnError(_lib.ERR_UNSUPPORTED, "norm %r" % (norm,))
+    across = norm == "layer_across_heads"
+    for w, n_ch in ((q_weight, H * D if across else D), (k_weight, Hk * D if across else D),
+                    (q_bias, H * D), (k_bias, Hk * D)):
+        if w is not None and (w.dtype != q.dtype or w.numel() != n_ch or not w.is_contiguous()):
+            raise DitAttnError(_lib.ERR_SHAPE, "norm weight/bias must be contiguous [%d] in the input dtype" % n_ch)
+    if not across and (q_bias is not None or k_bias is not None):
+        raise DitAttnError(_lib.ERR_UNSUPPORTED, "a bias needs norm='layer_across_heads'")
     dt = _dtype_code(q)
     if k.dtype != q.dtype or q_out.dtype != q.dtype or k_out.dtype != q.dtype:
         raise DitAttnError(_lib.ERR_UNSUPPORTED, "mixed dtypes")
     axes = (ctypes.c_int32 * len(axes_dims))(*[int(a) for a in axes_dims])
-    st = lib.dit_attn_qknorm_rope(q.data_ptr(), k.data_ptr(), q_out.data_ptr(), k_out.data_ptr(), _ptr(q_weight),
-                                  _ptr(k_weight), B, S, H, Hk, D, _bshd_strides(q, "q"), _bshd_strides(k, "k"),
-                                  _bshd_strides(q_out, "q_out"), _bshd_strides(k_out, "k_out"), pos_ids.data_ptr(),
-                                  len(axes_dims), axes, float(rope_theta), float(eps), float(q_scale), dt,
-                                  _stream(stream))
-    check(st, "dit_attn_qknorm_rope")
+    strides = (_bshd_strides(q, "q"), _bshd_strides(k, "k"), _bshd_strides(q_out, "q_out"),
+               _bshd_strides(k_out, "k_out"))
+    if not across and rope_linear_factor == 1.0 and rope_ntk_factor == 1.0:
+        st = lib.dit_attn_qknorm_rope(q.data_ptr(), k.data_ptr(), q_out.data_ptr(), k_out.data_ptr(), _ptr(q_weight),
+                                      _ptr(k_weight), B, S, H, Hk, D, *strides, pos_ids.data_ptr(), len(axes_dims),
+                                      axes, float(rope_theta), float(eps), float(q_scale), dt, _stream(stream))
+        check(st, "dit_attn_qknorm_rope")
+        return q_out, k_out
+    p = _lib.NormRopeParams(_NORM[norm], _ptr(q_weight), _ptr(k_weight), _ptr(q_bias), _ptr(k_bias), float(eps),
+                            float(rope_theta), float(rope_linear_factor), float(rope_ntk_factor), float(q_scale))
+    st = lib.dit_attn_qknorm_rope_ex(q.data_ptr(), k.data_ptr(), q_out.data_ptr(), k_out.data_ptr(), B, S, H, Hk, D,
+                                     *strides, pos_ids.data_ptr(), len(axes_dims), axes, ctypes.byref(p), dt,
+                                     _stream(stream))
+    check(st, "dit_attn_qknorm_rope_ex")
+    return q_out, k_out
+
+
+def dit_attn_qknorm_rope_ex(q, k, pos_ids, axes_dims, eps, norm="rms_per_head", q_weight=None, k_weight=None,
+                            q_bias=None, k_bias=None, rope_theta=10000.0, rope_linear_factor=1.0, rope_ntk_factor=1.0,
+                            q_scale=1.0, q_out=None, k_out=None, inplace=False, stream=None):
+    """Always through dit_attn_qknorm_rope_ex (even for the plain options)."""
+    if inplace:
+        q_out, k_out = q, k
+    if q_out is None:
+        q_out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if k_out is None:
+        k_out = torch.empty_like(k, memory_format=torch.contiguous_format)
+    B, S, H, D = q.shape
+    Hk = k.shape[2]
+    if k.shape[0] != B or k.shape[1] != S or k.shape[3] != D or q_out.shape != q.shape or k_out.shape != k.shape:
+        raise DitAttnError(_lib.ERR_SHAPE, "q/k/out shapes disagree")
+    if pos_ids.dtype != torch.int32 or not pos_ids.is_contiguous() or pos_ids.numel() < 3 * S:
+        raise DitAttnError(_lib.ERR_SHAPE, "pos_ids must be contiguous int32 [S, 3]")
+    dt = _dtype_code(q)
+    axes = (ctypes.c_int32 * len(axes_dims))(*[int(a) for a in axes_dims])
+    p = _lib.NormRopeParams(_NORM[norm], _ptr(q_weight), _ptr(k_weight), _ptr(q_bias), _ptr(k_bias), float(eps),
+                            float(rope_theta), float(rope_linear_factor), float(rope_ntk_factor), float(q_scale))
+    st = lib.dit_attn_qknorm_rope_ex(q.data_ptr(), k.data_ptr(), q_out.data_ptr(), k_out.data_ptr(), B, S, H, Hk, D,
+                                     _bshd_strides(q, "q"), _bshd_strides(k, "k"), _bshd_strides(q_out, "q_out"),
+                                     _bshd_strides(k_out, "k_out"), pos_ids.data_ptr(), len(axes_dims), axes,
+                                     ctypes.byref(p), dt, _stream(stream))
+    check(st, "dit_attn_qknorm_rope_ex")
     return q_out, k_out
 
 
@@ -283,6 +342,7 @@ def dit_attn_forward_cached_padded(q_new, k_cache, v_cache, k_new, v_new, key_va
 
 build_token_metadata = dit_attn_build_token_metadata
 build_key_valid = dit_attn_build_key_valid
+time_aware_rope_factors = dit_attn_time_aware_rope_factors
 qknorm_rope = dit_attn_qknorm_rope
 forward = dit_attn_forward
 forward_cached = dit_attn_forward_cached

@@ -112,22 +112,25 @@ int dit_attn_build_key_valid(const uint8_t* image_pad_mask, int32_t seq_len, con
   return e == hipSuccess ? DIT_ATTN_OK : DIT_ATTN_ERR_HIP;
 }
 
-int dit_attn_qknorm_rope(const void* q, const void* k, void* q_out, void* k_out, const void* q_weight,
-                         const void* k_weight, int32_t B, int32_t S, int32_t H, int32_t H_kv, int32_t D,
-                         const int64_t q_strides[3], const int64_t k_strides[3], const int64_t qo_strides[3],
-                         const int64_t ko_strides[3], const int32_t* pos_ids, int32_t n_axes,
-                         const int32_t* axes_dims, float rope_theta, float eps, float q_scale, int32_t dtype,
-                         void* stream) {
+static int qknorm_rope_common(const void* q, const void* k, void* q_out, void* k_out, int32_t B, int32_t S,
+                              int32_t H, int32_t H_kv, int32_t D, const int64_t q_strides[3],
+                              const int64_t k_strides[3], const int64_t qo_strides[3], const int64_t ko_strides[3],
+                              const int32_t* pos_ids, int32_t n_axes, const int32_t* axes_dims,
+                              const dit_attn_norm_rope_params& p, int32_t dtype, void* stream) {
   if (B < 0 || S < 0) return DIT_ATTN_ERR_SHAPE;
   if (B == 0 || S == 0) return DIT_ATTN_OK;  // nothing to do; no pointer is read
   if (!q || !k || !q_out || !k_out || !pos_ids || !axes_dims || !q_strides || !k_strides || !qo_strides ||
       !ko_strides)
     return DIT_ATTN_ERR_NULL;
   if (dtype != DIT_ATTN_BF16 && dtype != DIT_ATTN_F32) return DIT_ATTN_ERR_UNSUPPORTED;
-  if (B < 0 || S < 0 || H < 1 || H_kv < 1) return DIT_ATTN_ERR_SHAPE;
+  if (p.norm != DIT_ATTN_NORM_RMS_PER_HEAD && p.norm != DIT_ATTN_NORM_LAYER_ACROSS_HEADS)
+    return DIT_ATTN_ERR_UNSUPPORTED;
+  if (H < 1 || H_kv < 1) return DIT_ATTN_ERR_SHAPE;
   if (B > 65535) return DIT_ATTN_ERR_UNSUPPORTED;
   const int chunk = dtype == DIT_ATTN_BF16 ? 8 : 4;
   if (D < 8 || D > kMaxDim || D % chunk != 0) return DIT_ATTN_ERR_UNSUPPORTED;
+  if (p.norm == DIT_ATTN_NORM_LAYER_ACROSS_HEADS && (int64_t)(H + H_kv) * (D / chunk) > dit::kLayerNormMaxItems)
+    return DIT_ATTN_ERR_UNSUPPORTED;
   if (n_axes < 1 || n_axes > 3) return DIT_ATTN_ERR_SHAPE;
   int sum = 0;
   for (int i = 0; i < n_axes; ++i) {
@@ -135,15 +138,19 @@ int dit_attn_qknorm_rope(const void* q, const void* k, void* q_out, void* k_out,
     sum += axes_dims[i];
   }
   if (sum != D) return DIT_ATTN_ERR_SHAPE;
-  if (!(rope_theta > 0.f) || !std::isfinite(rope_theta) || !(eps >= 0.f) || !std::isfinite(eps) ||
-      !std::isfinite(q_scale) || q_scale == 0.f)
+  if (!(p.rope_theta > 0.f) || !std::isfinite(p.rope_theta) || !(p.eps >= 0.f) || !std::isfinite(p.eps) ||
+      !std::isfinite(p.q_scale) || p.q_scale == 0.f)
+    return DIT_ATTN_ERR_SHAPE;
+  if (!(p.rope_linear_factor > 0.f) || !std::isfinite(p.rope_linear_factor) || !(p.rope_ntk_factor > 0.f) ||
+      !std::isfinite(p.rope_ntk_factor))
     return DIT_ATTN_ERR_SHAPE;
   if (!strides_ok(q_strides) || !strides_ok(k_strides) || !strides_ok(qo_strides) || !strides_ok(ko_strides))
     return DIT_ATTN_ERR_SHAPE;
   const int es = elem_size(dtype);
   if (!rows_aligned(q, q_strides, es) || !rows_aligned(k, k_strides, es) || !rows_aligned(q_out, qo_strides, es) ||
-      !rows_aligned(k_out, ko_strides, es) || (q_weight && !aligned16(q_weight)) ||
-      (k_weight && !aligned16(k_weight)))
+      !rows_aligned(k_out, ko_strides, es) || (p.q_weight && !aligned16(p.q_weight)) ||
+      (p.k_weight && !aligned16(p.k_weight)) || (p.q_bias && !aligned16(p.q_bias)) ||
+      (p.k_bias && !aligned16(p.k_bias)))
     return DIT_ATTN_ERR_ALIGN;
 
   dit::QkNormRopeArgs a{};
@@ -151,8 +158,13 @@ int dit_attn_qknorm_rope(const void* q, const void* k, void* q_out, void* k_out,
   a.k = k;
   a.qo = q_out;
   a.ko = k_out;
-  a.wq = q_weight;
-  a.wk = k_weight;
+  a.wq = p.q_weight;
+  a.wk = p.k_weight;
+  a.norm = p.norm;
+  if (p.norm == DIT_ATTN_NORM_LAYER_ACROSS_HEADS) {
+    a.bq = p.q_bias;
+    a.bk = p.k_bias;
+  }
   a.pos = pos_ids;
   for (int i = 0; i < 3; ++i) {
     a.qs[i] = q_strides[i];
@@ -165,18 +177,68 @@ int dit_attn_qknorm_rope(const void* q, const void* k, void* q_out, void* k_out,
   a.H = H;
   a.Hk = H_kv;
   a.D = D;
-  a.eps = eps;
-  a.q_scale = q_scale;
-  int p = 0;
+  a.eps = p.eps;
+  a.q_scale = p.q_scale;
+  // Pair j of axis a turns by (pos / linear) * (theta * ntk)^(-2j/d_a): both
+  // factors fold into the pair's frequency.
+  const double base = (double)p.rope_theta * (double)p.rope_ntk_factor;
+  const double lin = (double)p.rope_linear_factor;
+  int pr = 0;
   for (int ax = 0; ax < n_axes; ++ax) {
     const int da = axes_dims[ax];
-    for (int j = 0; j < da / 2; ++j, ++p) {
-      a.omega[p] = std::pow((double)rope_theta, -2.0 * j / da);
-      a.pair_axis[p] = ax;
+    for (int j = 0; j < da / 2; ++j, ++pr) {
+      a.omega[pr] = std::pow(base, -2.0 * j / da) / lin;
+      a.pair_axis[pr] = ax;
     }
   }
   hipError_t e = dit::launch_qknorm_rope(a, dtype, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? DIT_ATTN_OK : DIT_ATTN_ERR_HIP;
+}
+
+int dit_attn_qknorm_rope(const void* q, const void* k, void* q_out, void* k_out, const void* q_weight,
+                         const void* k_weight, int32_t B, int32_t S, int32_t H, int32_t H_kv, int32_t D,
+                         const int64_t q_strides[3], const int64_t k_strides[3], const int64_t qo_strides[3],
+                         const int64_t ko_strides[3], const int32_t* pos_ids, int32_t n_axes,
+                         const int32_t* axes_dims, float rope_theta, float eps, float q_scale, int32_t dtype,
+                         void* stream) {
+  dit_attn_norm_rope_params p{};
+  p.norm = DIT_ATTN_NORM_RMS_PER_HEAD;
+  p.q_weight = q_weight;
+  p.k_weight = k_weight;
+  p.eps = eps;
+  p.rope_theta = rope_theta;
+  p.rope_linear_factor = 1.0f;
+  p.rope_ntk_factor = 1.0f;
+  p.q_scale = q_scale;
+  return qknorm_rope_common(q, k, q_out, k_out, B, S, H, H_kv, D, q_strides, k_strides, qo_strides, ko_strides,
+                            pos_ids, n_axes, axes_dims, p, dtype, stream);
+}
+
+int dit_attn_qknorm_rope_ex(const void* q, const void* k, void* q_out, void* k_out, int32_t B, int32_t S,
+                            int32_t H, int32_t H_kv, int32_t D, const int64_t q_strides[3],
+                            const int64_t k_strides[3], const int64_t qo_strides[3], const int64_t ko_strides[3],
+                            const int32_t* pos_ids, int32_t n_axes, const int32_t* axes_dims,
+                            const dit_attn_norm_rope_params* params, int32_t dtype, void* stream) {
+  if (B < 0 || S < 0) return DIT_ATTN_ERR_SHAPE;
+  if (B == 0 || S == 0) return DIT_ATTN_OK;
+  if (!params) return DIT_ATTN_ERR_NULL;
+  return qknorm_rope_common(q, k, q_out, k_out, B, S, H, H_kv, D, q_strides, k_strides, qo_strides, ko_strides,
+                            pos_ids, n_axes, axes_dims, *params, dtype, stream);
+}
+
+int dit_attn_time_aware_rope_factors(float t, float watershed, float scaling_factor, float* linear_factor,
+                                     float* ntk_factor) {
+  if (!linear_factor || !ntk_factor) return DIT_ATTN_ERR_NULL;
+  if (!(scaling_factor > 0.f) || !std::isfinite(scaling_factor) || !std::isfinite(t) || !std::isfinite(watershed))
+    return DIT_ATTN_ERR_SHAPE;
+  if (t < watershed) {
+    *linear_factor = scaling_factor;
+    *ntk_factor = 1.0f;
+  } else {
+    *linear_factor = 1.0f;
+    *ntk_factor = scaling_factor;
+  }
+  return DIT_ATTN_OK;
 }
 
 static int attention_common(const void* q, const void* kc, const void* vc, const void* kn, const void* vn, void* o,

@@ -42,8 +42,11 @@ struct QkNormRopeArgs {
   const void* k;
   void* qo;
   void* ko;
-  const void* wq;  // nullable: unit weight
+  const void* wq;  // nullable: unit weight ([D] per head, or [H*D] / [Hk*D] across heads)
   const void* wk;
+  const void* bq;  // nullable: zero bias (LayerNorm across heads only)
+  const void* bk;
+  int32_t norm;    // 0: RMSNorm per head; 1: LayerNorm across heads
   const int32_t* pos;  // [S][3]
   int64_t qs[3], ks[3], qos[3], kos[3];
   int32_t B, S, H, Hk, D;
@@ -54,6 +57,9 @@ struct QkNormRopeArgs {
 };
 
 hipError_t launch_qknorm_rope(const QkNormRopeArgs& a, int dtype, hipStream_t stream);
+
+// Most (head, chunk) items per token of the LayerNorm-across-heads kernel.
+constexpr int kLayerNormMaxItems = 2048;
 
 // Attention over a (possibly cached) key sequence.  Keys 0..P-1 come from the
 // cache pointers, keys P..P+Snew-1 from the new-token pointers; query row i is

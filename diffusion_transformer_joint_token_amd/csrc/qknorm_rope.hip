@@ -16,6 +16,16 @@
 // head's sum of squares is a butterfly over LPH lanes.  When a head's chunk
 // count is not a power of two (head_dim 72 in bf16: 9 chunks) a flat mapping
 // of (head, chunk) items over 1-4 tokens per work-group is used instead.
+//
+// Lumina-Next DiT article, section 3: with qk_norm its self-attention uses a
+// LayerNorm across heads instead -- one mean and variance over all of a
+// token's Q channels (and separately its K channels), then a per-channel
+// weight and bias.  qk_layernorm_rope_kernel handles that: one work-group per
+// token, (head, chunk) items dealt to the threads, mean and then centred
+// variance each reduced by wave butterflies and a fixed-order sum over the
+// waves (so results do not depend on timing).  The article's time-aware
+// rotary scaling (section 4) needs no kernel change: the host folds the
+// linear and NTK factors into each pair's frequency.
 
 #include "device_common.h"
 #include "kernels.h"
@@ -270,8 +280,165 @@ __global__ __launch_bounds__(kThreads) void qknorm_rope_flat_kernel(QkNormRopeAr
   }
 }
 
+// LayerNorm across heads: one token per work-group; item k of thread t is
+// (head, chunk) number t + 256 k, Q heads first.
+constexpr int kLnMaxItems = 8;
+
+// Sum of a Q partial and a K partial over the work-group, in a fixed order.
+__device__ __forceinline__ float2 block_sum2(float vq, float vk, float2 (*red)[kThreads / 64]) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    vq += __shfl_xor(vq, m, 64);
+    vk += __shfl_xor(vk, m, 64);
+  }
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) (*red)[wave] = make_float2(vq, vk);
+  __syncthreads();
+  float2 t = (*red)[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) {
+    t.x += (*red)[w].x;
+    t.y += (*red)[w].y;
+  }
+  return t;
+}
+
+template <typename T, int ITEMS>
+__global__ __launch_bounds__(kThreads) void qk_layernorm_rope_kernel(QkNormRopeArgs a) {
+  constexpr int EPC = Elem<T>::kPerChunk;
+  __shared__ float2 s_cs[kMaxPairs];
+  __shared__ float2 s_red[2][kThreads / 64];
+
+  const int tid = threadIdx.x;
+  const int s = blockIdx.x;
+  const int b = blockIdx.y;
+  const int D = a.D;
+  const int cph = D / EPC;
+  const int nq = a.H * cph;
+  const int n = (a.H + a.Hk) * cph;
+
+  u32x4 raw[ITEMS];
+#pragma unroll
+  for (int k = 0; k < ITEMS; ++k) {
+    const int item = tid + k * kThreads;
+    raw[k] = u32x4{0, 0, 0, 0};
+    if (item < n) {
+      const int vh = item / cph, c = item - vh * cph;
+      const T* src;
+      if (vh < a.H)
+        src = reinterpret_cast<const T*>(a.q) + b * a.qs[0] + (int64_t)s * a.qs[1] + vh * a.qs[2];
+      else
+        src = reinterpret_cast<const T*>(a.k) + b * a.ks[0] + (int64_t)s * a.ks[1] + (vh - a.H) * a.ks[2];
+      raw[k] = *reinterpret_cast<const u32x4*>(src + c * EPC);
+    }
+  }
+  if (tid < D / 2) {  // rotary phases of this token, as in the per-head kernel
+    const int ax = a.pair_axis[tid];
+    const double phase = (double)a.pos[3 * s + ax] * a.omega[tid];
+    const double turns = rint(phase * 0.15915494309189535);  // 1 / (2 pi)
+    const float red = (float)fma(-turns, 6.283185307179586, phase);
+    float sn, cs;
+    sincosf(red, &sn, &cs);
+    s_cs[tid] = make_float2(cs, sn);
+  }
+
+  // Mean of the token's Q channels and of its K channels.
+  float x[ITEMS][EPC];
+  float sq = 0.f, sk = 0.f;
+#pragma unroll
+  for (int k = 0; k < ITEMS; ++k) {
+    Elem<T>::unpack(raw[k], x[k]);
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < EPC; ++i) t += x[k][i];
+    if (tid + k * kThreads < nq) sq += t; else sk += t;  // items past n hold zeros
+  }
+  const float2 tot = block_sum2(sq, sk, &s_red[0]);
+  const float mq = tot.x / (float)(a.H * D), mk = tot.y / (float)(a.Hk * D);
+  // Centred variance.
+  float vq = 0.f, vk = 0.f;
+#pragma unroll
+  for (int k = 0; k < ITEMS; ++k) {
+    const int item = tid + k * kThreads;
+    if (item >= n) continue;
+    const float m = item < nq ? mq : mk;
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < EPC; ++i) {
+      const float d = x[k][i] - m;
+      t = fmaf(d, d, t);
+    }
+    if (item < nq) vq += t; else vk += t;
+  }
+  const float2 var = block_sum2(vq, vk, &s_red[1]);
+  const float rq = 1.0f / sqrtf(var.x / (float)(a.H * D) + a.eps);
+  const float rk = 1.0f / sqrtf(var.y / (float)(a.Hk * D) + a.eps);
+
+#pragma unroll
+  for (int k = 0; k < ITEMS; ++k) {
+    const int item = tid + k * kThreads;
+    if (item >= n) continue;
+    const int vh = item / cph, c = item - vh * cph;
+    const bool is_q = vh < a.H;
+    const int ch0 = (is_q ? vh : vh - a.H) * D + c * EPC;  // channel within the heads' span
+    float wv[EPC], bv[EPC];
+    {
+      const T* wp = reinterpret_cast<const T*>(is_q ? a.wq : a.wk);
+      const T* bp = reinterpret_cast<const T*>(is_q ? a.bq : a.bk);
+      if (wp != nullptr) {
+        Elem<T>::unpack(*reinterpret_cast<const u32x4*>(wp + ch0), wv);
+      } else {
+#pragma unroll
+        for (int i = 0; i < EPC; ++i) wv[i] = 1.0f;
+      }
+      if (bp != nullptr) {
+        Elem<T>::unpack(*reinterpret_cast<const u32x4*>(bp + ch0), bv);
+      } else {
+#pragma unroll
+        for (int i = 0; i < EPC; ++i) bv[i] = 0.0f;
+      }
+    }
+    const float m = is_q ? mq : mk, r = is_q ? rq : rk, sc = is_q ? a.q_scale : 1.0f;
+    float y[EPC];
+#pragma unroll
+    for (int i = 0; i < EPC; ++i) y[i] = fmaf((x[k][i] - m) * r, wv[i], bv[i]) * sc;
+#pragma unroll
+    for (int i = 0; i < EPC / 2; ++i) {
+      const float2 cs = s_cs[(c * EPC) / 2 + i];
+      const float y0 = y[2 * i], y1 = y[2 * i + 1];
+      y[2 * i] = y0 * cs.x - y1 * cs.y;
+      y[2 * i + 1] = y0 * cs.y + y1 * cs.x;
+    }
+    T* dst;
+    if (is_q)
+      dst = reinterpret_cast<T*>(a.qo) + b * a.qos[0] + (int64_t)s * a.qos[1] + vh * a.qos[2];
+    else
+      dst = reinterpret_cast<T*>(a.ko) + b * a.kos[0] + (int64_t)s * a.kos[1] + (vh - a.H) * a.kos[2];
+    *reinterpret_cast<u32x4*>(dst + c * EPC) = Elem<T>::pack(y);
+  }
+}
+
+template <typename T>
+hipError_t launch_layernorm(const QkNormRopeArgs& a, hipStream_t stream) {
+  constexpr int EPC = Elem<T>::kPerChunk;
+  const int n = (a.H + a.Hk) * (a.D / EPC);
+  const dim3 grid(a.S, a.B);
+  if (n <= kThreads)
+    hipLaunchKernelGGL((qk_layernorm_rope_kernel<T, 1>), grid, dim3(kThreads), 0, stream, a);
+  else if (n <= 2 * kThreads)
+    hipLaunchKernelGGL((qk_layernorm_rope_kernel<T, 2>), grid, dim3(kThreads), 0, stream, a);
+  else if (n <= 4 * kThreads)
+    hipLaunchKernelGGL((qk_layernorm_rope_kernel<T, 4>), grid, dim3(kThreads), 0, stream, a);
+  else if (n <= kLnMaxItems * kThreads)
+    hipLaunchKernelGGL((qk_layernorm_rope_kernel<T, kLnMaxItems>), grid, dim3(kThreads), 0, stream, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 template <typename T>
 hipError_t launch_typed(const QkNormRopeArgs& a, hipStream_t stream) {
+  if (a.norm == 1) return launch_layernorm<T>(a, stream);
   constexpr int EPC = Elem<T>::kPerChunk;
   const int chunks = a.D / EPC;
   const int per_tok = (a.H + a.Hk) * chunks;

@@ -19,7 +19,10 @@
  *      forward's kv_cache / kv_cache_mode);
  *   5. either attention with padded text keys left out, per sample
  *      (QwenImage21Transformer2DModel API page, forward's
- *      encoder_hidden_states_mask).
+ *      encoder_hidden_states_mask);
+ *   6. the Lumina-Next forms of step 2: LayerNorm across heads instead of the
+ *      per-head RMSNorm, and the time-aware rotary scaling (Lumina-Next DiT
+ *      article, sections 3 and 4).
  *
  * Conventions shared by every entry point
  *   - Memory: every pointer marked "device" is device memory owned by the
@@ -169,6 +172,56 @@ int dit_attn_qknorm_rope(const void *q, const void *k, void *q_out, void *k_out,
                          const int64_t qo_strides[3], const int64_t ko_strides[3],
                          const int32_t *pos_ids, int32_t n_axes, const int32_t *axes_dims,
                          float rope_theta, float eps, float q_scale, int32_t dtype, void *stream);
+
+/* Normalisation applied to Q and K before the rotary embedding. */
+typedef enum {
+  DIT_ATTN_NORM_RMS_PER_HEAD = 0,      /* y = x / sqrt(mean_D x^2 + eps) * w, w: [D] shared by the heads */
+  DIT_ATTN_NORM_LAYER_ACROSS_HEADS = 1 /* per token, over all heads' channels together:
+                                          y = (x - mean) / sqrt(var + eps) * w + b, biased variance,
+                                          w and b: [heads * D] (Lumina-Next DiT article, section 3) */
+} dit_attn_qk_norm;
+
+/* Options of dit_attn_qknorm_rope_ex (a host struct; its pointers are device
+ * buffers in the data dtype, 16-byte aligned, or NULL). */
+typedef struct {
+  int32_t norm;             /* dit_attn_qk_norm */
+  const void *q_weight;     /* RMS: [D]; LayerNorm: [H * D]; NULL = 1 */
+  const void *k_weight;     /* RMS: [D]; LayerNorm: [H_kv * D]; NULL = 1 */
+  const void *q_bias;       /* LayerNorm only: [H * D]; NULL = 0 (ignored for RMS) */
+  const void *k_bias;       /* LayerNorm only: [H_kv * D]; NULL = 0 */
+  float eps;                /* >= 0 */
+  float rope_theta;         /* rotary base, > 0 */
+  float rope_linear_factor; /* > 0: positions are divided by it (1 = none) */
+  float rope_ntk_factor;    /* > 0: the rotary base is multiplied by it (1 = none) */
+  float q_scale;            /* finite, != 0: multiplies the Q outputs (see dit_attn_qknorm_rope) */
+} dit_attn_norm_rope_params;
+
+/* dit_attn_qknorm_rope with a choice of norm and scaled rotary frequencies
+ * (Lumina-Next DiT article, section 3: qk_norm as a LayerNorm across heads;
+ * section 4: the rotary table rebuilt at every denoising step with a linear
+ * and an NTK factor).  Pair j of axis a turns by
+ * (pos / rope_linear_factor) * (rope_theta * rope_ntk_factor)^(-2j/d_a).
+ * With norm = RMS_PER_HEAD, both factors 1 and no bias the result is
+ * bit-identical to dit_attn_qknorm_rope.  The LayerNorm keeps separate
+ * statistics for Q (over H * D channels) and K (over H_kv * D channels), in
+ * fp32, reduced in a fixed order.  Limits: (H + H_kv) * D / 8 (bf16) or / 4
+ * (f32) <= 2048 for the LayerNorm; otherwise as dit_attn_qknorm_rope.
+ * params is a host pointer (NULL -> DIT_ATTN_ERR_NULL). */
+int dit_attn_qknorm_rope_ex(const void *q, const void *k, void *q_out, void *k_out,
+                            int32_t B, int32_t S, int32_t H, int32_t H_kv, int32_t D,
+                            const int64_t q_strides[3], const int64_t k_strides[3],
+                            const int64_t qo_strides[3], const int64_t ko_strides[3],
+                            const int32_t *pos_ids, int32_t n_axes, const int32_t *axes_dims,
+                            const dit_attn_norm_rope_params *params, int32_t dtype, void *stream);
+
+/* Host helper: the rotary factors of one denoising step (Lumina-Next DiT
+ * article, section 4).  t is the pipeline's reversed timestep (0 = noise,
+ * 1 = image).  Before the watershed (t < watershed) the linear factor is
+ * scaling_factor and the NTK factor 1; from it on the reverse.  (The page's
+ * comparison operator is lost from its text; this is the reading.)  Writes
+ * both outputs; errors: NULL outputs, non-finite inputs, scaling_factor <= 0. */
+int dit_attn_time_aware_rope_factors(float t, float watershed, float scaling_factor,
+                                     float *linear_factor, float *ntk_factor);
 
 /* Masked softmax attention (QwenImage21Transformer2DModel API page, block-causal
  * attention; NucleusMoE-Image article section 6.3 for GQA):

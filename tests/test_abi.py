@@ -174,3 +174,47 @@ def test_padded_attention_argument_errors():
     assert callc(kb=None) == _lib.ERR_NULL
     assert callc(kc=None) == _lib.ERR_NULL
     assert callc(words=1) == _lib.ERR_SHAPE             # 116 logical keys need 2 words
+
+
+def test_qknorm_rope_ex_argument_errors():
+    from diffusion_transformer_joint_token_amd import _lib
+    f = _lib.lib.dit_attn_qknorm_rope_ex
+    st = _s3(4096 * 40 * 72, 40 * 72, 72)
+    axes = (ctypes.c_int32 * 2)(36, 36)
+
+    def call(params, H=32, Hk=8, D=72, q=FAKE, B=2):
+        return f(q, FAKE, FAKE2, FAKE2, B, 4096, H, Hk, D, st, st, st, st, FAKE, 2, axes,
+                 ctypes.byref(params) if params is not None else None, 0, None)
+
+    def prm(**kw):
+        p = _lib.NormRopeParams(1, None, None, None, None, 1e-5, 1e4, 1.0, 1.0, 1.0)
+        for k, v in kw.items():
+            setattr(p, k, v)
+        return p
+    assert call(None) == _lib.ERR_NULL
+    assert call(prm(), q=None) == _lib.ERR_NULL
+    assert call(prm(norm=2)) == _lib.ERR_UNSUPPORTED
+    assert call(prm(rope_linear_factor=0.0)) == _lib.ERR_SHAPE
+    assert call(prm(rope_ntk_factor=-1.0)) == _lib.ERR_SHAPE
+    assert call(prm(rope_ntk_factor=float("inf"))) == _lib.ERR_SHAPE
+    assert call(prm(eps=-1.0)) == _lib.ERR_SHAPE
+    assert call(prm(q_bias=FAKE + 4)) == _lib.ERR_ALIGN
+    assert call(prm(), H=256, Hk=256, D=128) == _lib.ERR_UNSUPPORTED   # (256 + 256) * 16 chunks > 2048
+    assert call(prm(), B=0, q=None) == _lib.OK
+
+
+def test_time_aware_factors_host_helper():
+    """The C helper against the oracle's switch (the product's only host-side
+    arithmetic of the method), and its argument errors."""
+    import oracle.qknorm_rope as oqr
+    from diffusion_transformer_joint_token_amd import _lib
+    lin, ntk = ctypes.c_float(), ctypes.c_float()
+    for t in (0.0, 0.1, 0.29999, 0.3, 0.31, 0.7, 1.0):
+        for sf in (1.0, 2.0, 4.0):
+            assert _lib.lib.dit_attn_time_aware_rope_factors(t, 0.3, sf, ctypes.byref(lin), ctypes.byref(ntk)) == 0
+            ref = oqr.time_aware_rope_factors(float(ctypes.c_float(t).value), float(ctypes.c_float(0.3).value), sf)
+            assert (lin.value, ntk.value) == ref, (t, sf)
+    f = _lib.lib.dit_attn_time_aware_rope_factors
+    assert f(0.1, 0.3, 2.0, None, ctypes.byref(ntk)) == _lib.ERR_NULL
+    assert f(float("nan"), 0.3, 2.0, ctypes.byref(lin), ctypes.byref(ntk)) == _lib.ERR_SHAPE
+    assert f(0.1, 0.3, 0.0, ctypes.byref(lin), ctypes.byref(ntk)) == _lib.ERR_SHAPE

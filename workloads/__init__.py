@@ -55,6 +55,9 @@ class Workload:
     prefix_len: int = 0
     rope_theta: float = 10000.0
     description: str = ""
+    qk_norm: str = "rms_per_head"  # or "layer_across_heads" (weights and biases over heads x head_dim)
+    rope_linear: float = 1.0        # rotary linear factor (positions divided by it)
+    rope_ntk: float = 1.0           # rotary NTK factor (base multiplied by it)
 
     @property
     def seq_len(self) -> int:
@@ -101,6 +104,14 @@ VARIANTS: Dict[str, Workload] = {w.name: w for w in [
     Workload("nucleus_image_query_t1024_i64x64", 2, 16, 16, 128, (("T", 1024), ("I", 1, 64, 64)), (16, 56, 56),
              "centered_fhw", "full", 1e-6, "bf16", False, 5, prefix_len=1024,
              description="4096 image queries over 1024 cached text + 4096 image keys, full mask"),
+    # Lumina-Next at twice the trained resolution (Lumina-Next DiT article,
+    # section 3: qk_norm as a LayerNorm across heads; section 4: time-aware
+    # rotary scaling for resolution extrapolation): 2048 px -> a 128x128 token
+    # grid, scaling factor 2, a step past the watershed (NTK factor 2).
+    Workload("lumina_next_2k_lnheads_ntk2", 2, 32, 8, 72, (("I", 1, 128, 128),), (36, 36),
+             "grid_hw", "full", 1e-5, "bf16", False, 6,
+             description="CFG pair, 32 q / 8 kv heads x 72, 128x128 grid, LayerNorm across heads, NTK factor 2",
+             qk_norm="layer_across_heads", rope_ntk=2.0),
 ]}
 
 
@@ -114,10 +125,12 @@ def get(name_or_index) -> Workload:
 
 def small_workload(name: str, batch: int, heads: int, kv_heads: int, head_dim: int, layout,
                    axes, pos_mode="centered_fhw", mask_mode="block_causal", eps=1e-6,
-                   dtype="bf16", unit_weights=False, seed=0, prefix_len=0) -> Workload:
+                   dtype="bf16", unit_weights=False, seed=0, prefix_len=0, qk_norm="rms_per_head",
+                   rope_linear=1.0, rope_ntk=1.0) -> Workload:
     """A reduced workload of the same structure, for tests that must finish fast."""
     return Workload(name, batch, heads, kv_heads, head_dim, tuple(tuple(s) for s in layout), tuple(axes),
-                    pos_mode, mask_mode, eps, dtype, unit_weights, seed, prefix_len)
+                    pos_mode, mask_mode, eps, dtype, unit_weights, seed, prefix_len, qk_norm=qk_norm,
+                    rope_linear=rope_linear, rope_ntk=rope_ntk)
 
 
 def sequence_inputs(w: Workload) -> Tuple[np.ndarray, List[Tuple[int, int, int]]]:
@@ -195,14 +208,15 @@ def _store(d: Drawn, name: str, x32: np.ndarray) -> None:
         d.vals[name] = d.bits[name].astype(np.float64)
 
 
-def draw(w: Workload, parts: Sequence[str] = ("q", "k", "v", "wq", "wk", "k_cache", "v_cache")) -> Drawn:
+def draw(w: Workload, parts: Sequence[str] = ("q", "k", "v", "wq", "wk", "bq", "bk", "k_cache", "v_cache")) -> Drawn:
     """Seeded inputs in BSHD layout: rng = default_rng(seed); float32 standard
     normals drawn in the fixed order q, k, v (the query tokens: all tokens, or
     the tokens after the cached prefix), then the norm weights w_q, w_k
-    (1 + 0.02 N(0,1), unless unit), then the cached prefix K (already normed and
-    rotated) and raw V.  Each is rounded once to the workload dtype.  Drawing
-    always follows the full order so a subset of `parts` yields identical
-    values."""
+    (1 + 0.02 N(0,1), unless unit; [head_dim], or [heads x head_dim] for a
+    LayerNorm across heads, which then also draws biases b_q, b_k as
+    0.02 N(0,1)), then the cached prefix K (already normed and rotated) and
+    raw V.  Each is rounded once to the workload dtype.  Drawing always
+    follows the full order so a subset of `parts` yields identical values."""
     rng = np.random.default_rng(w.seed)
     B, S, H, Hk, D, P = w.batch, w.n_new, w.heads, w.kv_heads, w.head_dim, w.prefix_len
     d = Drawn(w)
@@ -211,13 +225,21 @@ def draw(w: Workload, parts: Sequence[str] = ("q", "k", "v", "wq", "wk", "k_cach
         x = rng.standard_normal(shapes[name], dtype=np.float32)
         if name in parts:
             _store(d, name, x)
+    across = w.qk_norm == "layer_across_heads"
     for name in ("wq", "wk"):
+        n_ch = ((H if name == "wq" else Hk) * D) if across else D
         if w.unit_weights:
-            x = np.ones((D,), np.float32)
+            x = np.ones((n_ch,), np.float32)
         else:
-            x = (1.0 + 0.02 * rng.standard_normal((D,), dtype=np.float32)).astype(np.float32)
+            x = (1.0 + 0.02 * rng.standard_normal((n_ch,), dtype=np.float32)).astype(np.float32)
         if name in parts:
             _store(d, name, x)
+    if across:  # LayerNorm biases, 0.02 N(0, 1)
+        for name in ("bq", "bk"):
+            n_ch = (H if name == "bq" else Hk) * D
+            x = (0.02 * rng.standard_normal((n_ch,), dtype=np.float32)).astype(np.float32)
+            if name in parts:
+                _store(d, name, x)
     if P > 0:
         for name in ("k_cache", "v_cache"):
             x = rng.standard_normal((B, P, Hk, D), dtype=np.float32)
