@@ -37,6 +37,10 @@ float64 NumPy, slow and plain:
   validity, which ``attention`` and ``attention_bruteforce`` take as
   ``key_valid`` (QwenImage21Transformer2DModel API page, ``forward``).
 
+* ``cfg.norm_rescaled_cfg`` -- classifier-free guidance whose mixed
+  prediction is rescaled, token by token, to the norm of the conditional one
+  (NucleusMoE-Image pipeline article, section 4.3).
+
 Pins: every function is pinned by tests under ``tests/`` that do not re-type
 its formula: closed forms, invariants (rotation preserves norms, relative
 phase), textbook special cases checked against library routines
@@ -46,4 +50,4 @@ inputs, and hand-derived token-metadata fixtures under ``tests/golden``.
 The pages print no numeric worked example for this step, so no pin is a
 printed value; none of the functions is left unpinned.
 """
-from . import metadata, qknorm_rope, attention, pipeline, key_padding  # noqa: F401
+from . import metadata, qknorm_rope, attention, pipeline, key_padding, cfg  # noqa: F401

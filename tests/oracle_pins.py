@@ -15,6 +15,7 @@ import numpy as np
 import torch
 
 import oracle.attention as att
+import oracle.cfg as ocfg
 import oracle.key_padding as kp
 import oracle.metadata as meta
 import oracle.qknorm_rope as qr
@@ -251,6 +252,36 @@ def pin_time_aware_factors():
     assert qr.time_aware_rope_factors(0.5, 0.3, 1.0) == (1.0, 1.0)
 
 
+# --------------------------------------------------------------------------- norm-rescaled CFG
+def pin_cfg_norm_rescale():
+    """NucleusMoE-Image article, section 4.3: every token's output has the
+    conditional prediction's norm and the mixed prediction's direction; scale 1
+    returns the conditional prediction, scale 0 the unconditional one rescaled;
+    a hand-worked token; a zero mixed prediction gives zero (reading)."""
+    rng = np.random.default_rng(41)
+    cond = rng.standard_normal((2, 9, 64))
+    unc = rng.standard_normal((2, 9, 64))
+    for g in (0.0, 1.0, 2.5, 7.0, -1.5):
+        out = ocfg.norm_rescaled_cfg(cond, unc, g)
+        comb = unc + g * (cond - unc)
+        assert np.allclose(np.linalg.norm(out, axis=-1), np.linalg.norm(cond, axis=-1), rtol=1e-13)
+        cos = np.sum(out * comb, axis=-1) / (np.linalg.norm(out, axis=-1) * np.linalg.norm(comb, axis=-1))
+        assert np.allclose(cos, 1.0, rtol=0, atol=1e-13)
+    assert np.allclose(ocfg.norm_rescaled_cfg(cond, unc, 1.0), cond, rtol=1e-13, atol=1e-14)
+    g0 = ocfg.norm_rescaled_cfg(cond, unc, 0.0)
+    assert np.allclose(g0, unc * (np.linalg.norm(cond, axis=-1) / np.linalg.norm(unc, axis=-1))[..., None],
+                       rtol=1e-13)
+    # cond (3, 4) (norm 5), uncond (1, 0), scale 2: mixed = (1, 0) + 2 * (2, 4) = (5, 8),
+    # norm sqrt(89); output = (5, 8) * 5 / sqrt(89).
+    out = ocfg.norm_rescaled_cfg([3.0, 4.0], [1.0, 0.0], 2.0)
+    assert np.allclose(out, np.array([5.0, 8.0]) * 5.0 / math.sqrt(89.0), rtol=0, atol=1e-15)
+    # homogeneous of degree 1 in (cond, uncond)
+    assert np.allclose(ocfg.norm_rescaled_cfg(3.0 * cond, 3.0 * unc, 4.0), 3.0 * ocfg.norm_rescaled_cfg(cond, unc, 4.0),
+                       rtol=1e-12)
+    z = ocfg.norm_rescaled_cfg(np.ones((1, 4)), np.ones((1, 4)) * 2.0, 2.0)  # mixed = 2 - 2 = 0 exactly
+    assert np.array_equal(z, np.zeros((1, 4)))
+
+
 # --------------------------------------------------------------------------- attention
 def pin_full_is_sdpa():
     """One image block and no text: the full mask and the block-causal mask both
@@ -484,4 +515,4 @@ ALL_PINS = [pin_metadata_goldens, pin_kv_limit_is_predicate_prefix, pin_metadata
             pin_singlepass_equals_multipass, pin_adjacent_blocks_stay_separate, pin_cached_equals_full,
             pin_bruteforce_tiny, pin_lse_definition, pin_key_padding_fixtures, pin_key_padding_is_masked_sdpa,
             pin_key_padding_is_compaction, pin_key_padding_bruteforce_and_empty_rows, pin_layernorm_across_heads,
-            pin_scaled_rope, pin_time_aware_factors]
+            pin_scaled_rope, pin_time_aware_factors, pin_cfg_norm_rescale]

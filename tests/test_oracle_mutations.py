@@ -4,6 +4,7 @@ import numpy as np
 import pytest
 
 import oracle.attention as att
+import oracle.cfg as ocfg
 import oracle.key_padding as kp
 import oracle.metadata as meta
 import oracle.qknorm_rope as qr
@@ -124,6 +125,32 @@ def _time_aware_swapped(t, watershed, scaling_factor):
     return (1.0, float(scaling_factor)) if t < watershed else (float(scaling_factor), 1.0)
 
 
+def _cfg_no_rescale(cond, uncond, guidance_scale):
+    # Mistake: plain CFG, the norm rescaling left out.
+    cond = np.asarray(cond, dtype=np.float64)
+    uncond = np.asarray(uncond, dtype=np.float64)
+    return uncond + guidance_scale * (cond - uncond)
+
+
+def _rescaled(comb, ref):
+    return comb * (np.linalg.norm(ref, axis=-1, keepdims=True) / np.linalg.norm(comb, axis=-1, keepdims=True))
+
+
+def _cfg_rescale_to_uncond(cond, uncond, guidance_scale):
+    # Mistake: rescaled to the unconditional prediction's norm.
+    cond = np.asarray(cond, dtype=np.float64)
+    uncond = np.asarray(uncond, dtype=np.float64)
+    return _rescaled(uncond + guidance_scale * (cond - uncond), uncond)
+
+
+def _cfg_swapped_mix(cond, uncond, guidance_scale):
+    # Mistake: mixed as cond + scale * (uncond - cond).
+    cond = np.asarray(cond, dtype=np.float64)
+    uncond = np.asarray(uncond, dtype=np.float64)
+    return _rescaled(cond + guidance_scale * (uncond - cond), cond)
+
+
+cfg_orig = ocfg.norm_rescaled_cfg
 qr_rope_orig = qr.rope
 att_attention_orig = att.attention
 
@@ -237,6 +264,9 @@ MUTATIONS = [
     ("layernorm_per_head", qr, "layer_norm_across_heads", _ln_per_head),
     ("layernorm_without_centering", qr, "layer_norm_across_heads", _ln_no_centering),
     ("time_aware_branches_swapped", qr, "time_aware_rope_factors", _time_aware_swapped),
+    ("cfg_without_rescale", ocfg, "norm_rescaled_cfg", _cfg_no_rescale),
+    ("cfg_rescaled_to_uncond_norm", ocfg, "norm_rescaled_cfg", _cfg_rescale_to_uncond),
+    ("cfg_mix_direction_swapped", ocfg, "norm_rescaled_cfg", _cfg_swapped_mix),
 ]
 
 
