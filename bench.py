@@ -40,6 +40,8 @@ PEAK_HBM_GBS = 8000.0
 DEFAULT_WORKLOAD = "qwen_image21_t1024_i64x64"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_hbm_traffic.json")
 ATTN_SOURCE = os.path.join(ROOT, "diffusion_transformer_joint_token_amd", "csrc", "attn_fwd.hip")
+CFG_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "cfg_norm_rescale_hbm_traffic.json")
+CFG_SOURCE = os.path.join(ROOT, "diffusion_transformer_joint_token_amd", "csrc", "cfg.hip")
 
 
 def log(msg: str) -> None:
@@ -72,15 +74,15 @@ def source_sha(path: str) -> str:
         return hashlib.sha256(fh.read()).hexdigest()
 
 
-def measured_traffic(w: wl.Workload):
-    """HBM bytes per attention launch from the committed rocprofv3 counter runs,
-    or None when they were taken on another kernel source or workload."""
+def measured_traffic(w, path: str = TRAFFIC_FILE, source: str = ATTN_SOURCE):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, or None
+    when they were taken on another kernel source or workload."""
     try:
-        with open(TRAFFIC_FILE) as fh:
+        with open(path) as fh:
             rec = json.load(fh)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha256") != source_sha(ATTN_SOURCE) or rec.get("workload") != w.name:
+    if rec.get("kernel_source_sha256") != source_sha(source) or rec.get("workload") != w.name:
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -300,6 +302,81 @@ def cpu_baseline(w: wl.Workload, drawn: wl.Drawn, budget_s: float = 12.0, text_v
             "seconds": elapsed}
 
 
+def bench_cfg(name: str, steps: int, warmup: int, cpu_budget: float, no_cpu: bool) -> dict:
+    """The norm-rescaled guidance step on its own: `steps` back-to-back
+    launches rotating over enough (cond, uncond, out) copies that one launch's
+    data were not touched by the launches just before it (more than the 256 MB
+    Infinity Cache).  One pair of HIP events on the launch stream brackets all
+    of them (a pair per launch would add about 2 us to a 12 us kernel); the
+    per-launch pairs of a second pass give the median and minimum."""
+    import torch
+    import diffusion_transformer_joint_token_amd as dit
+    w = wl.CFG_WORKLOADS[name]
+    bits, vals = wl.draw_cfg(w.rows, w.channels, w.seed, w.dtype)
+
+    def dev(x):
+        if w.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    elem = 2 if w.dtype == "bf16" else 4
+    per_call = 3 * w.rows * w.channels * elem           # read cond + uncond, write out
+    copies = max(2, -(-(512 << 20) // per_call))        # > 2x the Infinity Cache in flight
+    conds = [dev(bits["cond"]) for _ in range(copies)]
+    uncs = [dev(bits["uncond"]) for _ in range(copies)]
+    outs = [torch.empty_like(conds[0]) for _ in range(copies)]
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        dit.cfg_norm_rescale(conds[i % copies], uncs[i % copies], w.guidance, out=outs[i % copies])
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(steps):
+        dit.cfg_norm_rescale(conds[i % copies], uncs[i % copies], w.guidance, out=outs[i % copies])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_mean = t0.elapsed_time(t1) / steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i, (a, b) in enumerate(ev):
+        a.record(stream)
+        dit.cfg_norm_rescale(conds[i % copies], uncs[i % copies], w.guidance, out=outs[i % copies])
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in ev]
+    gbs = per_call / (ms_mean * 1e-3) / 1e9
+    line = {
+        "metric": "norm-rescaled CFG GB/s (HBM bytes moved per second)", "value": gbs, "unit": "GB/s",
+        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": ms_mean, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "rows": w.rows, "channels": w.channels, "guidance": w.guidance,
+                   "step": "uncond + s (cond - uncond), rescaled per token to ||cond||"},
+        "per_launch_events": {"ms_median": float(np.median(ms)), "ms_min": float(np.min(ms))},
+        "rotated_copies": copies,
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": gbs / PEAK_HBM_GBS, "traffic": measured_traffic(w, CFG_TRAFFIC_FILE, CFG_SOURCE),
+                     "kernel": "cfg_norm_rescale_kernel",
+                     "bytes_per_launch": per_call, "launch_ms_mean": ms_mean},
+        "cpu_baseline": None,
+    }
+    if not no_cpu:
+        import oracle.cfg as ocfg
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        except Exception:  # noqa: BLE001
+            threads = len(os.sched_getaffinity(0))
+        rng = np.random.default_rng(0)
+        t0, done = time.perf_counter(), 0
+        while time.perf_counter() - t0 < cpu_budget:
+            r0 = int(rng.integers(0, w.rows - 4096))
+            ocfg.norm_rescaled_cfg(vals["cond"][r0:r0 + 4096], vals["uncond"][r0:r0 + 4096], w.guidance)
+            done += 4096
+        el = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": 3 * done * w.channels * elem / el / 1e9, "unit": "GB/s",
+                                "cores": int(threads), "kind": "oracle",
+                                "sample": "%d rows (blocks of 4096) of %s, %.1f s" % (done, w.name, el)}
+    return line
+
+
 def _counter_rows(path: str):
     import csv
     import glob
@@ -321,6 +398,24 @@ def _per_dispatch(rows, kernel_substr: str, counter: str) -> float:
     if not per:
         raise SystemExit("counter %s not found for kernel %s" % (counter, kernel_substr))
     return sum(per.values()) / len(per)
+
+
+def summarize_cfg_counters(root: str, copy_mib: int, workload: str) -> int:
+    """CPU only: FETCH_SIZE / WRITE_SIZE of the guidance kernel (runs fetch/
+    and write/ under root) scaled by the copy calibration runs (copy_fetch/,
+    copy_write/), written as the traffic record bench.py --cfg reads."""
+    fetch = _per_dispatch(_counter_rows(os.path.join(root, "fetch")), "cfg_norm_rescale", "FETCH_SIZE")
+    write = _per_dispatch(_counter_rows(os.path.join(root, "write")), "cfg_norm_rescale", "WRITE_SIZE")
+    cf = _per_dispatch(_counter_rows(os.path.join(root, "copy_fetch")), "copyBuffer", "FETCH_SIZE")
+    cw = _per_dispatch(_counter_rows(os.path.join(root, "copy_write")), "copyBuffer", "WRITE_SIZE")
+    copy_kib = copy_mib * 1024.0
+    fs, ws = copy_kib / cf, copy_kib / cw
+    rec = {"kernel": "cfg_norm_rescale_kernel", "workload": workload, "kernel_source_sha256": source_sha(CFG_SOURCE),
+           "copy_bytes": copy_mib << 20, "copy_fetch_kib": cf, "copy_write_kib": cw, "fetch_scale": fs,
+           "write_scale": ws, "fetch_bytes": fetch * fs * 1024.0, "write_bytes": write * ws * 1024.0}
+    rec["hbm_bytes_per_launch"] = rec["fetch_bytes"] + rec["write_bytes"]
+    print(json.dumps(rec, indent=1, sort_keys=True))
+    return 0
 
 
 def summarize_counters(root: str, copy_mib: int, workload: str) -> int:
@@ -371,6 +466,8 @@ def main(argv=None) -> int:
     ap.add_argument("--text-padding", default="none", choices=["none", "right", "random"],
                     help="pad the text per sample (seeded text mask: 'right' keeps a random-length prefix, "
                          "'random' a coin per token) and run the padded attention entry points")
+    ap.add_argument("--cfg", default=None, choices=list(wl.CFG_WORKLOADS),
+                    help="benchmark the norm-rescaled guidance step on this workload instead (own JSON line)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (the reference "
@@ -380,6 +477,8 @@ def main(argv=None) -> int:
     args = ap.parse_args(argv)
 
     if args.summarize_counters:
+        if args.cfg:
+            return summarize_cfg_counters(args.summarize_counters, args.copy_calibration or 256, args.cfg)
         return summarize_counters(args.summarize_counters, args.copy_calibration or 256, args.workload)
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
@@ -389,6 +488,11 @@ def main(argv=None) -> int:
     if not torch.cuda.is_available():
         print("bench.py needs an MI355X GPU (none visible)", file=sys.stderr)
         return 2
+
+    if args.cfg:
+        print(json.dumps(bench_cfg(args.cfg, args.steps, args.warmup, args.cpu_budget, args.no_cpu_baseline)),
+              flush=True)
+        return 0
 
     if args.copy_calibration:
         n = args.copy_calibration << 20

@@ -20,8 +20,8 @@ __all__ = ["TokenMeta", "KeyValid", "DitAttnError", "LN2", "LOG2E", "prescaled_q
            "dit_attn_build_token_metadata", "dit_attn_build_key_valid", "dit_attn_qknorm_rope",
            "dit_attn_qknorm_rope_ex", "dit_attn_time_aware_rope_factors", "dit_attn_forward",
            "dit_attn_forward_cached", "dit_attn_forward_padded", "dit_attn_forward_cached_padded",
-           "build_token_metadata", "build_key_valid", "qknorm_rope", "time_aware_rope_factors", "forward",
-           "forward_cached"]
+           "dit_attn_cfg_norm_rescale", "build_token_metadata", "build_key_valid", "qknorm_rope",
+           "time_aware_rope_factors", "forward", "forward_cached", "cfg_norm_rescale"]
 
 _POS = {"centered_fhw": _lib.POS_CENTERED_FHW, "grid_hw": _lib.POS_GRID_HW}
 
@@ -340,7 +340,38 @@ def dit_attn_forward_cached_padded(q_new, k_cache, v_cache, k_new, v_new, key_va
                                    return_lse, stream, key_valid=key_valid)
 
 
+def _rows(t: torch.Tensor, name: str) -> Tuple[torch.Tensor, int]:
+    """t as [rows, C] with a single row stride (a view), and that stride."""
+    if t.dim() < 1 or t.stride(-1) != 1 and t.shape[-1] > 1:
+        raise DitAttnError(_lib.ERR_SHAPE, "%s: channels must be contiguous" % name)
+    try:
+        v = t.view(-1, t.shape[-1])
+    except RuntimeError:
+        raise DitAttnError(_lib.ERR_SHAPE, "%s: rows must share one stride" % name) from None
+    return v, (v.stride(0) if v.shape[0] > 1 else v.shape[1])
+
+
+def dit_attn_cfg_norm_rescale(cond: torch.Tensor, uncond: torch.Tensor, guidance_scale: float,
+                              out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Norm-rescaled classifier-free guidance over the last axis (one row per
+    token); out may be cond or uncond (in place)."""
+    if uncond.shape != cond.shape:
+        raise DitAttnError(_lib.ERR_SHAPE, "cond and uncond shapes differ")
+    if out is None:
+        out = torch.empty_like(cond, memory_format=torch.contiguous_format)
+    if out.shape != cond.shape or any(t.dtype != cond.dtype for t in (uncond, out)):
+        raise DitAttnError(_lib.ERR_SHAPE, "out must match cond in shape and dtype")
+    c2, cs = _rows(cond, "cond")
+    u2, us = _rows(uncond, "uncond")
+    o2, os_ = _rows(out, "out")
+    st = lib.dit_attn_cfg_norm_rescale(c2.data_ptr(), u2.data_ptr(), o2.data_ptr(), c2.shape[0], c2.shape[1], cs, us,
+                                       os_, float(guidance_scale), _dtype_code(cond), _stream(stream))
+    check(st, "dit_attn_cfg_norm_rescale")
+    return out
+
+
 build_token_metadata = dit_attn_build_token_metadata
+cfg_norm_rescale = dit_attn_cfg_norm_rescale
 build_key_valid = dit_attn_build_key_valid
 time_aware_rope_factors = dit_attn_time_aware_rope_factors
 qknorm_rope = dit_attn_qknorm_rope

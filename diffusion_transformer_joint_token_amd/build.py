@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libdit_attn.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["token_meta.hip", "qknorm_rope.hip", "attn_fwd.hip", "api.cpp"]
+SOURCES = ["token_meta.hip", "qknorm_rope.hip", "attn_fwd.hip", "cfg.hip", "api.cpp"]
 
 ARCH = "gfx950"
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",

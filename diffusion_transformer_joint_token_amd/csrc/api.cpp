@@ -358,4 +358,35 @@ int dit_attn_forward_cached_padded(const void* q_new, const void* k_cache, const
                           meta, key_valid, key_valid_stride, softmax_scale, dtype, stream);
 }
 
+int dit_attn_cfg_norm_rescale(const void* cond, const void* uncond, void* out, int64_t rows, int32_t channels,
+                              int64_t cond_stride, int64_t uncond_stride, int64_t out_stride, float guidance_scale,
+                              int32_t dtype, void* stream) {
+  if (rows < 0 || channels < 1) return DIT_ATTN_ERR_SHAPE;
+  if (rows == 0) return DIT_ATTN_OK;  // nothing to do; no pointer is read
+  if (!cond || !uncond || !out) return DIT_ATTN_ERR_NULL;
+  if (dtype != DIT_ATTN_BF16 && dtype != DIT_ATTN_F32) return DIT_ATTN_ERR_UNSUPPORTED;
+  const int chunk = dtype == DIT_ATTN_BF16 ? 8 : 4;
+  if (channels % chunk != 0) return DIT_ATTN_ERR_UNSUPPORTED;
+  if (channels / chunk > 64 * 8) return DIT_ATTN_ERR_UNSUPPORTED;
+  if (!std::isfinite(guidance_scale)) return DIT_ATTN_ERR_SHAPE;
+  if (cond_stride < channels || uncond_stride < channels || out_stride < channels) return DIT_ATTN_ERR_SHAPE;
+  if (rows > (int64_t)INT32_MAX * 8) return DIT_ATTN_ERR_UNSUPPORTED;
+  const int es = elem_size(dtype);
+  if (!aligned16(cond) || !aligned16(uncond) || !aligned16(out) || (cond_stride * es) % 16 ||
+      (uncond_stride * es) % 16 || (out_stride * es) % 16)
+    return DIT_ATTN_ERR_ALIGN;
+  dit::CfgArgs a{};
+  a.cond = cond;
+  a.uncond = uncond;
+  a.out = out;
+  a.rows = rows;
+  a.cs = cond_stride;
+  a.us = uncond_stride;
+  a.os = out_stride;
+  a.C = channels;
+  a.g = guidance_scale;
+  hipError_t e = dit::launch_cfg_norm_rescale(a, dtype, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DIT_ATTN_OK : DIT_ATTN_ERR_HIP;
+}
+
 }  // extern "C"

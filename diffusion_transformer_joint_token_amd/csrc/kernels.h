@@ -82,4 +82,16 @@ struct AttnArgs {
 
 hipError_t launch_attention(const AttnArgs& a, int dtype, hipStream_t stream);
 
+// Norm-rescaled classifier-free guidance over rows of C channels.
+struct CfgArgs {
+  const void* cond;
+  const void* uncond;
+  void* out;
+  int64_t rows, cs, us, os;  // row count; row strides in elements
+  int32_t C;
+  float g;                   // guidance scale
+};
+
+hipError_t launch_cfg_norm_rescale(const CfgArgs& a, int dtype, hipStream_t stream);
+
 }  // namespace dit

@@ -22,7 +22,10 @@
  *      encoder_hidden_states_mask);
  *   6. the Lumina-Next forms of step 2: LayerNorm across heads instead of the
  *      per-head RMSNorm, and the time-aware rotary scaling (Lumina-Next DiT
- *      article, sections 3 and 4).
+ *      article, sections 3 and 4);
+ *   7. outside the attention: the norm-rescaled classifier-free guidance that
+ *      combines the conditional and unconditional predictions of a step
+ *      (NucleusMoE-Image pipeline article, section 4.3).
  *
  * Conventions shared by every entry point
  *   - Memory: every pointer marked "device" is device memory owned by the
@@ -288,6 +291,24 @@ int dit_attn_forward_cached_padded(const void *q_new, const void *k_cache, const
                                    const dit_attn_token_meta *meta, const uint64_t *key_valid,
                                    int64_t key_valid_stride, float softmax_scale, int32_t dtype,
                                    void *stream);
+
+/* Classifier-free guidance with norm rescaling (NucleusMoE-Image pipeline
+ * article, section 4.3), row by row (a row = one token's C channels):
+ *   mix = uncond + guidance_scale * (cond - uncond)
+ *   out = mix * ||cond|| / ||mix||        (norms over the row's channels)
+ * A row whose mix is exactly zero is written as zero.  Arithmetic in fp32,
+ * one rounding on the store.
+ *   cond, uncond, out  device [rows][channels] in dtype; row r starts at
+ *                      ptr + r * stride (strides in elements, >= channels);
+ *                      channels contiguous.  out may alias cond or uncond
+ *                      exactly (same pointer and stride).
+ *   channels           a multiple of 8 (bf16) or 4 (f32), at most 4096 (bf16)
+ *                      or 2048 (f32).  guidance_scale finite.
+ * rows == 0 returns DIT_ATTN_OK at once.  Base pointers and strides keep rows
+ * 16-byte aligned. */
+int dit_attn_cfg_norm_rescale(const void *cond, const void *uncond, void *out, int64_t rows,
+                              int32_t channels, int64_t cond_stride, int64_t uncond_stride,
+                              int64_t out_stride, float guidance_scale, int32_t dtype, void *stream);
 
 /* Static description of a status code (never NULL). */
 const char *dit_attn_status_string(int32_t status);

@@ -218,3 +218,21 @@ def test_time_aware_factors_host_helper():
     assert f(0.1, 0.3, 2.0, None, ctypes.byref(ntk)) == _lib.ERR_NULL
     assert f(float("nan"), 0.3, 2.0, ctypes.byref(lin), ctypes.byref(ntk)) == _lib.ERR_SHAPE
     assert f(0.1, 0.3, 0.0, ctypes.byref(lin), ctypes.byref(ntk)) == _lib.ERR_SHAPE
+
+
+def test_cfg_argument_errors():
+    from diffusion_transformer_joint_token_amd import _lib
+    f = _lib.lib.dit_attn_cfg_norm_rescale
+
+    def call(c=FAKE, u=FAKE2, o=FAKE2, rows=4096, C=64, cs=64, us=64, os_=64, g=4.0, dtype=0):
+        return f(c, u, o, rows, C, cs, us, os_, g, dtype, None)
+    assert call(c=None) == _lib.ERR_NULL
+    assert call(C=60) == _lib.ERR_UNSUPPORTED          # not a multiple of 8 (bf16)
+    assert call(C=8 * 513) == _lib.ERR_UNSUPPORTED     # more than 4096 bf16 channels
+    assert call(cs=32) == _lib.ERR_SHAPE               # rows overlap
+    assert call(g=float("nan")) == _lib.ERR_SHAPE
+    assert call(C=0) == _lib.ERR_SHAPE
+    assert call(dtype=3) == _lib.ERR_UNSUPPORTED
+    assert call(u=FAKE2 + 8) == _lib.ERR_ALIGN
+    assert call(cs=68) == _lib.ERR_ALIGN               # 136-byte row stride
+    assert call(rows=0, c=None) == _lib.OK

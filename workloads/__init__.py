@@ -25,7 +25,7 @@ from typing import Dict, List, Sequence, Tuple
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "VARIANTS", "get", "sequence_inputs", "draw", "bf16_round_bits",
+__all__ = ["Workload", "WORKLOADS", "VARIANTS", "CfgWorkload", "CFG_WORKLOADS", "draw_cfg", "get", "sequence_inputs", "draw", "bf16_round_bits",
            "bf16_bits_to_f64", "small_workload", "n_text_tokens", "text_mask"]
 
 
@@ -113,6 +113,54 @@ VARIANTS: Dict[str, Workload] = {w.name: w for w in [
              description="CFG pair, 32 q / 8 kv heads x 72, 128x128 grid, LayerNorm across heads, NTK factor 2",
              qk_norm="layer_across_heads", rope_ntk=2.0),
 ]}
+
+
+@dataclass(frozen=True)
+class CfgWorkload:
+    """The guidance step of a denoising step: the conditional and unconditional
+    predictions of `batch` images of `tokens` tokens with `channels` channels
+    each (NucleusMoE-Image pipeline article, section 4.3; section 1 and the
+    transformer configuration of section 6 for 1024 px -> 64x64 tokens of
+    64 packed latent channels; guidance_scale 4.0 is the pipeline default)."""
+    name: str
+    batch: int
+    tokens: int
+    channels: int
+    guidance: float
+    dtype: str
+    seed: int
+    description: str = ""
+
+    @property
+    def rows(self) -> int:
+        return self.batch * self.tokens
+
+
+CFG_WORKLOADS: Dict[str, CfgWorkload] = {w.name: w for w in [
+    CfgWorkload("nucleus_cfg_b32_1024px", 32, 4096, 64, 4.0, "bf16", 7,
+                description="32 images at 1024 px: 131072 tokens x 64 channels, guidance 4.0"),
+]}
+
+
+def draw_cfg(rows: int, channels: int, seed: int, dtype: str = "bf16"):
+    """Seeded (cond, uncond) predictions [rows, channels] as (bits, vals)
+    dicts like `draw`: rng = default_rng(seed); float32 base, d1, d2 standard
+    normals drawn in that order; cond = base + 0.3 d1, uncond = base + 0.3 d2
+    (two predictions of one step agree on most of their content); each
+    rounded once to the dtype."""
+    rng = np.random.default_rng(seed)
+    base = rng.standard_normal((rows, channels), dtype=np.float32)
+    d1 = rng.standard_normal((rows, channels), dtype=np.float32)
+    d2 = rng.standard_normal((rows, channels), dtype=np.float32)
+    bits, vals = {}, {}
+    for name, x in (("cond", base + np.float32(0.3) * d1), ("uncond", base + np.float32(0.3) * d2)):
+        if dtype == "bf16":
+            b = bf16_round_bits(x)
+            bits[name], vals[name] = b, bf16_bits_to_f64(b)
+        else:
+            bits[name] = np.ascontiguousarray(x, dtype=np.float32)
+            vals[name] = bits[name].astype(np.float64)
+    return bits, vals
 
 
 def get(name_or_index) -> Workload:
