@@ -29,7 +29,9 @@
 //    chunk) and the transposed V reads (4 rows x 4 chunks) hit distinct banks.
 //  * Softmax in the exp2 domain; the running max is only moved when a row's
 //    new maximum exceeds it by more than 8 (log2 units), so O is rarely
-//    rescaled and probabilities stay <= 2^8.
+//    rescaled and probabilities stay <= 2^8.  Every S tile's accumulator
+//    starts from one register tile holding -offset, rebuilt only when the
+//    offset moves (the first QK^T MFMA reads it as its C operand).
 //  * All query tiles of one (batch, head) run on one XCD (and its L2); the
 //    light low query tiles of each XCD go out last.
 //  * Padded text keys (same page, forward's encoder_hidden_states_mask): one
@@ -308,22 +310,22 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   const float c2 = a.scale * 1.4426950408889634f;  // scale * log2(e); 1 when UNIT
   const float ic2 = UNIT ? 1.0f : 1.0f / c2;
   float m_off = 0.f;   // running offset (log2 units)
+  // Every S tile's accumulator starts here: -m_off in logit units, rebuilt only
+  // when the offset moves.
+  f32x16 s_init;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s_init[i] = -m_off * ic2;
   bool fresh = true;   // no finite logit seen yet: the first one sets the offset
   float l_part = 0.f;  // this lane's share of the row sum
 
   // S^T (logits minus the offset, logit units) for the 64 keys of a K stage.
   auto qk = [&](const char* kt, f32x16 (&sacc)[2]) __attribute__((always_inline)) {
-    const float init = -m_off * ic2;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[kb][i] = init;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const bf16x8 kop = *reinterpret_cast<const bf16x8*>(kt + k_off[ks] + kb * 32 * kRowBytes);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[ks], sacc[kb], 0, 0, 0);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[ks], ks == 0 ? s_init : sacc[kb], 0, 0, 0);
       }
     }
   };
@@ -364,6 +366,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) sacc[kb] -= d;
       m_off += d * c2;
+      const float ni = -m_off * ic2;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s_init[i] = ni;
     }
     // Without padding every row's first tile holds key 0, which it may see.
     if constexpr (PADDED)
