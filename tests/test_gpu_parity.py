@@ -120,6 +120,46 @@ def test_metadata_goldens_and_random_layouts(dit):
             assert np.array_equal(got, ref[key].astype(got.dtype)), (layout, key)
 
 
+def test_metadata_long_misaligned_and_chunk_errors(dit):
+    """Many 1024-token chunks (prefix counts across chunks), the mask at an odd
+    byte offset (the byte-load path of the count), and layout errors whose
+    evidence lies in a later chunk than the block's start."""
+    rng = np.random.default_rng(77)
+    for trial in range(6):
+        segs, n = [], 0
+        while n < 18000:
+            if rng.random() < 0.45:
+                segs.append(("T", int(rng.integers(1, 1500))))
+                n += segs[-1][1]
+            else:
+                f, hh, ww = int(rng.integers(1, 3)), 2 * int(rng.integers(1, 30)), 2 * int(rng.integers(1, 30))
+                segs.append(("I", f, hh, ww))
+                n += f * hh * ww
+        w = wl.small_workload("m", 1, 1, 1, 8, tuple(segs), (8,))
+        mask, shapes = wl.sequence_inputs(w)
+        ref = ometa.build_token_metadata(mask, shapes, "centered_fhw")
+        for offset in (0, 1, 3):
+            buf = torch.zeros(mask.size + 16, dtype=torch.uint8, device="cuda")
+            buf[offset:offset + mask.size] = torch.from_numpy(mask).cuda()
+            m = dit.build_token_metadata(buf[offset:offset + mask.size], shapes, "centered_fhw")
+            m.check()
+            for key in ("image_ids", "target_mask", "pos_ids", "kv_limit"):
+                got = getattr(m, key).cpu().numpy()
+                assert np.array_equal(got, ref[key].astype(got.dtype)), (trial, offset, key)
+
+    def status(mask, shapes):
+        m = dit.build_token_metadata(torch.tensor(mask, dtype=torch.uint8).cuda(), shapes)
+        torch.cuda.synchronize()
+        return int(m.status.item())
+    # one 40x40 block (1600 tokens) split by a text token at position 1500: the
+    # gap sits in the second chunk
+    mask = [1] * 1500 + [0] + [1] * 100
+    assert status(mask, [(1, 40, 40)]) == 5
+    assert status([1] * 1600 + [0], [(1, 40, 40)]) == 0
+    # a count error one token past a chunk boundary
+    assert status([0] * 1024 + [1] * 5, [(1, 2, 2)]) == 5
+
+
 def test_metadata_data_errors(dit):
     def status(mask, shapes, mode="centered_fhw"):
         m = dit.build_token_metadata(torch.tensor(mask, dtype=torch.uint8).cuda(), shapes, mode)
