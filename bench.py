@@ -2,9 +2,13 @@
 """Benchmark of the joint text+image DiT attention step on one MI355X.
 
 A step is one pass of the whole path on one batch of synthetic inputs that
-are already resident in HBM: token metadata -> fused QK-RMSNorm + rotary ->
-masked attention (the cached-prefix workload runs the cached attention entry
-point instead of the plain one).  Default workload: batch 2, 32 heads x 128,
+are already resident in HBM: token metadata -> QK-RMSNorm + rotary -> masked
+attention (the cached-prefix workload runs the cached attention entry point
+instead of the plain one).  For bf16 with the per-head RMSNorm, Q's norm,
+rotary embedding and softmax scale run inside the attention kernel as it
+loads Q (dit_attn_forward_cached_qnorm) and the norm kernel handles K alone;
+--unfused-q times the two-kernel form (the norm kernel writes Q' to HBM and
+the attention reads it back).  Default workload: batch 2, 32 heads x 128,
 1024 text tokens followed by one 1x64x64 target image block (5120 tokens),
 block-causal mask, bf16.
 
@@ -90,10 +94,12 @@ def measured_traffic(w, path: str = TRAFFIC_FILE, source: str = ATTN_SOURCE):
 class Step:
     """Device buffers and the launch sequence of one step."""
 
-    def __init__(self, w: wl.Workload, device, text_padding: str = "none"):
+    def __init__(self, w: wl.Workload, device, text_padding: str = "none", fuse_q: bool = True):
         import torch
         import diffusion_transformer_joint_token_amd as dit
         self.torch, self.dit, self.w = torch, dit, w
+        # Q's norm inside the attention kernel: bf16, per-head RMSNorm only.
+        self.fused = fuse_q and w.dtype == "bf16" and w.qk_norm == "rms_per_head"
         d = wl.draw(w)
         self.drawn = d
 
@@ -122,7 +128,7 @@ class Step:
             self.tv_dev = torch.from_numpy(self.tv).to(device)
             self.kv = dit.KeyValid(torch.empty(w.batch, (w.seq_len + 63) // 64, dtype=torch.int64, device=device),
                                    torch.empty(1, dtype=torch.int32, device=device))
-        self.qp = torch.empty_like(self.q)
+        self.qp = None if self.fused else torch.empty_like(self.q)
         self.kp = torch.empty_like(self.k)
         self.o = torch.empty_like(self.q)
         self.stream = torch.cuda.current_stream()
@@ -132,16 +138,40 @@ class Step:
         if self.kv is not None:
             self.dit.build_key_valid(self.mask, self.tv_dev, out=self.kv)
 
+    def norm_launch(self, q, k, pos_ids, qp, kp):
+        """The norm kernel on (q, k).  Fused: K only.  Otherwise Q' and K',
+        with the softmax scale and log2(e) folded into Q' (one rounding), so
+        the attention exponentiates its MFMA output directly."""
+        w = self.w
+        if self.fused:
+            self.dit.dit_attn_qknorm_rope_ex(None, k, pos_ids, w.axes, w.eps, k_weight=self.wk, k_out=kp,
+                                             rope_theta=w.rope_theta, **self.norm_kw)
+        else:
+            self.dit.qknorm_rope(q, k, pos_ids, w.axes, w.eps, self.wq, self.wk, q_out=qp, k_out=kp,
+                                 q_scale=self.dit.prescaled_q_factor(w.head_dim), **self.norm_kw)
+
+    def attention_launch(self, q, qp, k_cache, v_cache, kp, v, out, pos_ids):
+        w = self.w
+        if self.fused:
+            self.dit.forward_cached_qnorm(q, k_cache, v_cache, kp, v, pos_ids, w.axes, w.eps, q_weight=self.wq,
+                                          rope_theta=w.rope_theta, rope_linear_factor=w.rope_linear,
+                                          rope_ntk_factor=w.rope_ntk, mask_mode=w.mask_mode, meta=self.meta,
+                                          out=out, key_valid=self.kv)
+        elif k_cache is not None:
+            self.dit.forward_cached(qp, k_cache, v_cache, kp, v, w.mask_mode, self.meta,
+                                    softmax_scale=self.dit.LN2, out=out, key_valid=self.kv)
+        else:
+            self.dit.forward(qp, kp, v, w.mask_mode, self.meta, softmax_scale=self.dit.LN2, out=out,
+                             key_valid=self.kv)
+
     def norm_rope(self):
-        # The softmax scale and log2(e) are folded into Q' here (one rounding),
-        # so the attention exponentiates its MFMA output directly.
-        P = self.w.prefix_len
-        self.dit.qknorm_rope(self.q, self.k, self.meta.pos_ids[P:], self.w.axes, self.w.eps, self.wq, self.wk,
-                             q_out=self.qp, k_out=self.kp, q_scale=self.dit.prescaled_q_factor(self.w.head_dim),
-                             **self.norm_kw)
+        self.norm_launch(self.q, self.k, self.meta.pos_ids[self.w.prefix_len:], self.qp, self.kp)
 
     def attention(self):
-        if self.w.prefix_len:
+        if self.fused:
+            self.attention_launch(self.q, None, self.kc, self.vc, self.kp, self.v, self.o,
+                                  self.meta.pos_ids[self.w.prefix_len:])
+        elif self.w.prefix_len:
             self.dit.forward_cached(self.qp, self.kc, self.vc, self.kp, self.v, self.w.mask_mode, self.meta,
                                     softmax_scale=self.dit.LN2, out=self.o, key_valid=self.kv)
         else:
@@ -187,15 +217,13 @@ def time_norm_cold(step: Step, reps: int = 30, copies: int = 3):
     by one launch were not touched by the launches just before it (config
     3's Q+K, 168 MB, would otherwise partly stay in the 256 MB Infinity
     Cache)."""
-    torch, dit, w = step.torch, step.dit, step.w
+    torch, w = step.torch, step.w
     P = w.prefix_len
     qs = [step.q] + [step.q.clone() for _ in range(copies - 1)]
     ks = [step.k] + [step.k.clone() for _ in range(copies - 1)]
-    scale = dit.prescaled_q_factor(w.head_dim)
 
     def launch(i):
-        dit.qknorm_rope(qs[i % copies], ks[i % copies], step.meta.pos_ids[P:], w.axes, w.eps, step.wq, step.wk,
-                        q_out=step.qp, k_out=step.kp, q_scale=scale, **step.norm_kw)
+        step.norm_launch(qs[i % copies], ks[i % copies], step.meta.pos_ids[P:], step.qp, step.kp)
     for i in range(copies):
         launch(i)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
@@ -227,16 +255,12 @@ def multistep(step: Step, n_steps: int, reps: int, warmup: int, full_ms: float):
         raise SystemExit("--multistep needs a workload with tokens before the target block and no cache of its own")
     q_new, k_new, v_new = step.q[:, P:], step.k[:, P:], step.v[:, P:]
     k_cache, v_cache = step.kp[:, :P], step.v[:, :P]
-    qp_new = torch.empty_like(q_new, memory_format=torch.contiguous_format)
+    qp_new = None if step.fused else torch.empty_like(q_new, memory_format=torch.contiguous_format)
     kp_new = torch.empty_like(k_new, memory_format=torch.contiguous_format)
     o_new = torch.empty_like(q_new, memory_format=torch.contiguous_format)
-    scale = dit.prescaled_q_factor(w.head_dim)
-
     def cached():
-        dit.qknorm_rope(q_new, k_new, step.meta.pos_ids[P:], w.axes, w.eps, step.wq, step.wk,
-                        q_out=qp_new, k_out=kp_new, q_scale=scale, **step.norm_kw)
-        dit.forward_cached(qp_new, k_cache, v_cache, kp_new, v_new, w.mask_mode, step.meta,
-                           softmax_scale=dit.LN2, out=o_new, key_valid=step.kv)
+        step.norm_launch(q_new, k_new, step.meta.pos_ids[P:], qp_new, kp_new)
+        step.attention_launch(q_new, qp_new, k_cache, v_cache, kp_new, v_new, o_new, step.meta.pos_ids[P:])
     step.run()
     for _ in range(warmup):
         cached()
@@ -468,6 +492,9 @@ def main(argv=None) -> int:
                          "'random' a coin per token) and run the padded attention entry points")
     ap.add_argument("--cfg", default=None, choices=list(wl.CFG_WORKLOADS),
                     help="benchmark the norm-rescaled guidance step on this workload instead (own JSON line)")
+    ap.add_argument("--unfused-q", action="store_true",
+                    help="two-kernel form: the norm kernel writes Q' and the attention reads it (default for bf16 "
+                         "with the per-head RMSNorm: Q's norm and rotation inside the attention kernel)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (the reference "
@@ -519,7 +546,7 @@ def main(argv=None) -> int:
         w = dataclasses.replace(w, name="%s_textpad_%s" % (w.name, args.text_padding))
     log("workload %s: B=%d H=%d/%d D=%d S=%d (queries %d) mask=%s dtype=%s" % (
         w.name, w.batch, w.heads, w.kv_heads, w.head_dim, w.seq_len, w.n_new, w.mask_mode, w.dtype))
-    step = Step(w, "cuda", args.text_padding)
+    step = Step(w, "cuda", args.text_padding, fuse_q=not args.unfused_q)
     step.run()
     torch.cuda.synchronize()
     step.meta.check()
@@ -541,12 +568,16 @@ def main(argv=None) -> int:
     value = flops / (t["step_ms"] * 1e-3) / 1e12
     attn_tflops = flops / (t["attn_ms_mean"] * 1e-3) / 1e12
     elem = 2 if w.dtype == "bf16" else 4
-    norm_bytes = 2 * w.batch * w.n_new * (w.heads + w.kv_heads) * w.head_dim * elem
+    # Norm kernel traffic: read + write of the heads it norms.
+    normed_heads = w.kv_heads if step.fused else w.heads + w.kv_heads
+    norm_bytes = 2 * w.batch * w.n_new * normed_heads * w.head_dim * elem
 
     roofline = {"bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": attn_tflops / PEAK_BF16_TFLOPS, "traffic": measured_traffic(w),
-                "kernel": "attn_fwd_bf16_kernel<%d,4%s>" % ((w.head_dim + 31) // 32 * 32,
-                                                            ",padded" if step.kv is not None else ""), "launch_ms_mean": t["attn_ms_mean"],
+                "kernel": "attn_fwd_bf16_kernel<%d,4%s%s>" % ((w.head_dim + 31) // 32 * 32,
+                                                              ",padded" if step.kv is not None else "",
+                                                              ",qnorm" if step.fused else ""),
+                "launch_ms_mean": t["attn_ms_mean"],
                 "launch_ms_min": t["attn_ms_min"], "flops_per_launch": flops}
     line = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -557,12 +588,13 @@ def main(argv=None) -> int:
                    "rope_axes": list(w.axes), "qk_norm": w.qk_norm, "rope_linear_factor": w.rope_linear,
                    "rope_ntk_factor": w.rope_ntk,
                    "step": "token metadata + qk-%s/rope + attention" % (
-                       "rmsnorm" if w.qk_norm == "rms_per_head" else "layernorm-across-heads")},
+                       "rmsnorm" if w.qk_norm == "rms_per_head" else "layernorm-across-heads"),
+                   "q_norm": "inside the attention kernel" if step.fused else "norm kernel (Q' through HBM)"},
         "pct_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
         "attention_only": {"tflops": attn_tflops, "pct_bf16_peak": 100.0 * attn_tflops / PEAK_BF16_TFLOPS,
                            "ms_mean": t["attn_ms_mean"], "ms_median": t["attn_ms_median"],
                            "ms_min": t["attn_ms_min"]},
-        "qknorm_rope": {"ms": t["norm_ms"], "gbs": norm_bytes / (t["norm_ms"] * 1e-3) / 1e9,
+        "qknorm_rope": {"heads": "k only" if step.fused else "q and k", "ms": t["norm_ms"], "gbs": norm_bytes / (t["norm_ms"] * 1e-3) / 1e9,
                         "frac_hbm": norm_bytes / (t["norm_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
                         "bytes": norm_bytes,
                         "rotated_inputs": {"copies": 3, "ms_mean": cold["ms_mean"], "ms_median": cold["ms_median"],

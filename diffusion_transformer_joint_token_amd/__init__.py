@@ -10,7 +10,8 @@ implementation behind these names.
 """
 from .api import (LN2, LOG2E, DitAttnError, KeyValid, TokenMeta, build_key_valid,  # noqa: F401
                   build_token_metadata, cfg_norm_rescale, dit_attn_build_key_valid, dit_attn_cfg_norm_rescale, dit_attn_build_token_metadata, dit_attn_forward,
-                  dit_attn_forward_cached, dit_attn_forward_cached_padded, dit_attn_forward_padded,
+                  dit_attn_forward_cached, dit_attn_forward_cached_padded, dit_attn_forward_cached_qnorm,
+                  dit_attn_forward_padded,
                   dit_attn_qknorm_rope, dit_attn_qknorm_rope_ex, dit_attn_time_aware_rope_factors, forward,
-                  forward_cached, prescaled_q_factor, qknorm_rope, time_aware_rope_factors)
+                  forward_cached, forward_cached_qnorm, prescaled_q_factor, qknorm_rope, time_aware_rope_factors)
 from ._lib import LIB_PATH  # noqa: F401

@@ -20,8 +20,8 @@ __all__ = ["TokenMeta", "KeyValid", "DitAttnError", "LN2", "LOG2E", "prescaled_q
            "dit_attn_build_token_metadata", "dit_attn_build_key_valid", "dit_attn_qknorm_rope",
            "dit_attn_qknorm_rope_ex", "dit_attn_time_aware_rope_factors", "dit_attn_forward",
            "dit_attn_forward_cached", "dit_attn_forward_padded", "dit_attn_forward_cached_padded",
-           "dit_attn_cfg_norm_rescale", "build_token_metadata", "build_key_valid", "qknorm_rope",
-           "time_aware_rope_factors", "forward", "forward_cached", "cfg_norm_rescale"]
+           "dit_attn_forward_cached_qnorm", "dit_attn_cfg_norm_rescale", "build_token_metadata", "build_key_valid", "qknorm_rope",
+           "time_aware_rope_factors", "forward", "forward_cached", "forward_cached_qnorm", "cfg_norm_rescale"]
 
 _POS = {"centered_fhw": _lib.POS_CENTERED_FHW, "grid_hw": _lib.POS_GRID_HW}
 
@@ -224,25 +224,31 @@ def dit_attn_qknorm_rope(q: torch.Tensor, k: torch.Tensor, pos_ids: torch.Tensor
 def dit_attn_qknorm_rope_ex(q, k, pos_ids, axes_dims, eps, norm="rms_per_head", q_weight=None, k_weight=None,
                             q_bias=None, k_bias=None, rope_theta=10000.0, rope_linear_factor=1.0, rope_ntk_factor=1.0,
                             q_scale=1.0, q_out=None, k_out=None, inplace=False, stream=None):
-    """Always through dit_attn_qknorm_rope_ex (even for the plain options)."""
+    """Always through dit_attn_qknorm_rope_ex (even for the plain options).
+    q=None norms K alone and returns (None, k_out): the form that goes with
+    dit_attn_forward_cached_qnorm, which norms Q itself."""
     if inplace:
         q_out, k_out = q, k
-    if q_out is None:
+    if q is not None and q_out is None:
         q_out = torch.empty_like(q, memory_format=torch.contiguous_format)
     if k_out is None:
         k_out = torch.empty_like(k, memory_format=torch.contiguous_format)
-    B, S, H, D = q.shape
-    Hk = k.shape[2]
-    if k.shape[0] != B or k.shape[1] != S or k.shape[3] != D or q_out.shape != q.shape or k_out.shape != k.shape:
+    B, S, Hk, D = k.shape
+    H = 0 if q is None else q.shape[2]
+    if q is not None and (q.shape[0] != B or q.shape[1] != S or q.shape[3] != D or q_out.shape != q.shape):
         raise DitAttnError(_lib.ERR_SHAPE, "q/k/out shapes disagree")
+    if k_out.shape != k.shape:
+        raise DitAttnError(_lib.ERR_SHAPE, "k_out must match k")
     if pos_ids.dtype != torch.int32 or not pos_ids.is_contiguous() or pos_ids.numel() < 3 * S:
         raise DitAttnError(_lib.ERR_SHAPE, "pos_ids must be contiguous int32 [S, 3]")
-    dt = _dtype_code(q)
+    dt = _dtype_code(k)
     axes = (ctypes.c_int32 * len(axes_dims))(*[int(a) for a in axes_dims])
     p = _lib.NormRopeParams(_NORM[norm], _ptr(q_weight), _ptr(k_weight), _ptr(q_bias), _ptr(k_bias), float(eps),
                             float(rope_theta), float(rope_linear_factor), float(rope_ntk_factor), float(q_scale))
-    st = lib.dit_attn_qknorm_rope_ex(q.data_ptr(), k.data_ptr(), q_out.data_ptr(), k_out.data_ptr(), B, S, H, Hk, D,
-                                     _bshd_strides(q, "q"), _bshd_strides(k, "k"), _bshd_strides(q_out, "q_out"),
+    zero = _lib.Strides3(0, 0, 0)
+    st = lib.dit_attn_qknorm_rope_ex(_ptr(q), k.data_ptr(), _ptr(q_out), k_out.data_ptr(), B, S, H, Hk, D,
+                                     _bshd_strides(q, "q") if q is not None else zero, _bshd_strides(k, "k"),
+                                     _bshd_strides(q_out, "q_out") if q is not None else zero,
                                      _bshd_strides(k_out, "k_out"), pos_ids.data_ptr(), len(axes_dims), axes,
                                      ctypes.byref(p), dt, _stream(stream))
     check(st, "dit_attn_qknorm_rope_ex")
@@ -340,6 +346,60 @@ def dit_attn_forward_cached_padded(q_new, k_cache, v_cache, k_new, v_new, key_va
                                    return_lse, stream, key_valid=key_valid)
 
 
+def dit_attn_forward_cached_qnorm(q_raw: torch.Tensor, k_cache: Optional[torch.Tensor],
+                                  v_cache: Optional[torch.Tensor], k_new: torch.Tensor, v_new: torch.Tensor,
+                                  pos_ids: torch.Tensor, axes_dims: Sequence[int], eps: float,
+                                  q_weight: Optional[torch.Tensor] = None, rope_theta: float = 10000.0,
+                                  rope_linear_factor: float = 1.0, rope_ntk_factor: float = 1.0,
+                                  q_scale: float = 1.0, mask_mode: Union[str, int] = "block_causal",
+                                  meta: Optional[TokenMeta] = None, softmax_scale: Optional[float] = None,
+                                  out: Optional[torch.Tensor] = None, return_lse: bool = False, stream=None,
+                                  key_valid=None):
+    """Attention on raw Q: the kernel applies Q's per-head RMSNorm (weight
+    q_weight), its rotary embedding (positions pos_ids [S_new, 3] of the query
+    tokens, i.e. meta.pos_ids[P:]) and the softmax scale as it loads Q.  K
+    must be normed and rotated already (dit_attn_qknorm_rope_ex with q=None).
+    k_cache=None is the plain (uncached) form; key_valid as forward_cached."""
+    B, S_new, H, D = q_raw.shape
+    Hk = k_new.shape[2]
+    P = 0 if k_cache is None else k_cache.shape[1]
+    if k_new.shape != (B, S_new, Hk, D) or v_new.shape != (B, S_new, Hk, D):
+        raise DitAttnError(_lib.ERR_SHAPE, "k_new/v_new must be [B, S_new, H_kv, D]")
+    if P > 0 and (k_cache.shape != (B, P, Hk, D) or v_cache is None or v_cache.shape != (B, P, Hk, D)):
+        raise DitAttnError(_lib.ERR_SHAPE, "k_cache/v_cache must be [B, P, H_kv, D]")
+    if pos_ids.dtype != torch.int32 or not pos_ids.is_contiguous() or pos_ids.numel() < 3 * S_new:
+        raise DitAttnError(_lib.ERR_SHAPE, "pos_ids must be contiguous int32 [S_new, 3]")
+    if q_weight is not None and (q_weight.dtype != q_raw.dtype or q_weight.numel() != D
+                                 or not q_weight.is_contiguous()):
+        raise DitAttnError(_lib.ERR_SHAPE, "q_weight must be contiguous [%d] in the input dtype" % D)
+    o = out if out is not None else torch.empty_like(q_raw, memory_format=torch.contiguous_format)
+    lse = _lse_buffer(return_lse, B, H, S_new, q_raw.device)
+    zero = _lib.Strides3(0, 0, 0)
+    strides = (_lib.Strides3 * 6)(_bshd_strides(q_raw, "q_raw"),
+                                  _bshd_strides(k_cache, "k_cache") if P > 0 else zero,
+                                  _bshd_strides(v_cache, "v_cache") if P > 0 else zero,
+                                  _bshd_strides(k_new, "k_new"), _bshd_strides(v_new, "v_new"),
+                                  _bshd_strides(o, "out"))
+    dt = _dtype_code(q_raw)
+    if any(t.dtype != q_raw.dtype for t in (k_new, v_new, o)):
+        raise DitAttnError(_lib.ERR_UNSUPPORTED, "mixed dtypes")
+    mode = _MASK[mask_mode] if isinstance(mask_mode, str) else int(mask_mode)
+    ms = meta.struct() if meta is not None else None
+    msp = ctypes.byref(ms) if ms is not None else None
+    scale = 0.0 if softmax_scale is None else float(softmax_scale)
+    kc, vc = (_ptr(k_cache), _ptr(v_cache)) if P > 0 else (None, None)
+    kb, kbs = _key_bits(key_valid) if key_valid is not None else (None, 0)
+    axes = (ctypes.c_int32 * len(axes_dims))(*[int(a) for a in axes_dims])
+    p = _lib.NormRopeParams(_lib.NORM_RMS_PER_HEAD, _ptr(q_weight), None, None, None, float(eps), float(rope_theta),
+                            float(rope_linear_factor), float(rope_ntk_factor), float(q_scale))
+    st = lib.dit_attn_forward_cached_qnorm(q_raw.data_ptr(), kc, vc, k_new.data_ptr(), v_new.data_ptr(),
+                                           o.data_ptr(), _ptr(lse), B, P, S_new, H, Hk, D, strides, mode, msp, kb,
+                                           kbs, pos_ids.data_ptr(), len(axes_dims), axes, ctypes.byref(p), scale,
+                                           dt, _stream(stream))
+    check(st, "dit_attn_forward_cached_qnorm")
+    return (o, lse) if return_lse else o
+
+
 def _rows(t: torch.Tensor, name: str) -> Tuple[torch.Tensor, int]:
     """t as [rows, C] with a single row stride (a view), and that stride."""
     if t.dim() < 1 or t.stride(-1) != 1 and t.shape[-1] > 1:
@@ -377,3 +437,4 @@ time_aware_rope_factors = dit_attn_time_aware_rope_factors
 qknorm_rope = dit_attn_qknorm_rope
 forward = dit_attn_forward
 forward_cached = dit_attn_forward_cached
+forward_cached_qnorm = dit_attn_forward_cached_qnorm

@@ -112,25 +112,13 @@ int dit_attn_build_key_valid(const uint8_t* image_pad_mask, int32_t seq_len, con
   return e == hipSuccess ? DIT_ATTN_OK : DIT_ATTN_ERR_HIP;
 }
 
-static int qknorm_rope_common(const void* q, const void* k, void* q_out, void* k_out, int32_t B, int32_t S,
-                              int32_t H, int32_t H_kv, int32_t D, const int64_t q_strides[3],
-                              const int64_t k_strides[3], const int64_t qo_strides[3], const int64_t ko_strides[3],
-                              const int32_t* pos_ids, int32_t n_axes, const int32_t* axes_dims,
-                              const dit_attn_norm_rope_params& p, int32_t dtype, void* stream) {
-  if (B < 0 || S < 0) return DIT_ATTN_ERR_SHAPE;
-  if (B == 0 || S == 0) return DIT_ATTN_OK;  // nothing to do; no pointer is read
-  if (!q || !k || !q_out || !k_out || !pos_ids || !axes_dims || !q_strides || !k_strides || !qo_strides ||
-      !ko_strides)
-    return DIT_ATTN_ERR_NULL;
-  if (dtype != DIT_ATTN_BF16 && dtype != DIT_ATTN_F32) return DIT_ATTN_ERR_UNSUPPORTED;
-  if (p.norm != DIT_ATTN_NORM_RMS_PER_HEAD && p.norm != DIT_ATTN_NORM_LAYER_ACROSS_HEADS)
-    return DIT_ATTN_ERR_UNSUPPORTED;
-  if (H < 1 || H_kv < 1) return DIT_ATTN_ERR_SHAPE;
-  if (B > 65535) return DIT_ATTN_ERR_UNSUPPORTED;
-  const int chunk = dtype == DIT_ATTN_BF16 ? 8 : 4;
-  if (D < 8 || D > kMaxDim || D % chunk != 0) return DIT_ATTN_ERR_UNSUPPORTED;
-  if (p.norm == DIT_ATTN_NORM_LAYER_ACROSS_HEADS && (int64_t)(H + H_kv) * (D / chunk) > dit::kLayerNormMaxItems)
-    return DIT_ATTN_ERR_UNSUPPORTED;
+// Rotary frequencies: pair j of axis a turns by (pos / linear) *
+// (theta * ntk)^(-2j/d_a) radians; both factors fold into the pair's
+// frequency, stored in turns (divided by 2 pi) for the kernels' reduction.
+// Validates the axes (each even, summing to D) and the factors.
+static int rope_frequencies(int32_t D, int32_t n_axes, const int32_t* axes_dims, float theta, float linear,
+                            float ntk, double* omega, int32_t* pair_axis) {
+  if (!axes_dims) return DIT_ATTN_ERR_NULL;
   if (n_axes < 1 || n_axes > 3) return DIT_ATTN_ERR_SHAPE;
   int sum = 0;
   for (int i = 0; i < n_axes; ++i) {
@@ -138,22 +126,59 @@ static int qknorm_rope_common(const void* q, const void* k, void* q_out, void* k
     sum += axes_dims[i];
   }
   if (sum != D) return DIT_ATTN_ERR_SHAPE;
-  if (!(p.rope_theta > 0.f) || !std::isfinite(p.rope_theta) || !(p.eps >= 0.f) || !std::isfinite(p.eps) ||
-      !std::isfinite(p.q_scale) || p.q_scale == 0.f)
+  if (!(theta > 0.f) || !std::isfinite(theta) || !(linear > 0.f) || !std::isfinite(linear) || !(ntk > 0.f) ||
+      !std::isfinite(ntk))
     return DIT_ATTN_ERR_SHAPE;
-  if (!(p.rope_linear_factor > 0.f) || !std::isfinite(p.rope_linear_factor) || !(p.rope_ntk_factor > 0.f) ||
-      !std::isfinite(p.rope_ntk_factor))
+  const double base = (double)theta * (double)ntk;
+  int pr = 0;
+  for (int ax = 0; ax < n_axes; ++ax) {
+    const int da = axes_dims[ax];
+    for (int j = 0; j < da / 2; ++j, ++pr) {
+      omega[pr] = std::pow(base, -2.0 * j / da) / (double)linear / 6.283185307179586476925;
+      pair_axis[pr] = ax;
+    }
+  }
+  return DIT_ATTN_OK;
+}
+
+static int qknorm_rope_common(const void* q, const void* k, void* q_out, void* k_out, int32_t B, int32_t S,
+                              int32_t H, int32_t H_kv, int32_t D, const int64_t q_strides[3],
+                              const int64_t k_strides[3], const int64_t qo_strides[3], const int64_t ko_strides[3],
+                              const int32_t* pos_ids, int32_t n_axes, const int32_t* axes_dims,
+                              const dit_attn_norm_rope_params& p, int32_t dtype, void* stream) {
+  if (B < 0 || S < 0) return DIT_ATTN_ERR_SHAPE;
+  if (B == 0 || S == 0) return DIT_ATTN_OK;  // nothing to do; no pointer is read
+  // Q may be left out (both q and q_out NULL): K only.
+  const bool has_q = q != nullptr || q_out != nullptr;
+  if ((has_q && (!q || !q_out || !q_strides || !qo_strides)) || !k || !k_out || !pos_ids || !axes_dims ||
+      !k_strides || !ko_strides)
+    return DIT_ATTN_ERR_NULL;
+  if (dtype != DIT_ATTN_BF16 && dtype != DIT_ATTN_F32) return DIT_ATTN_ERR_UNSUPPORTED;
+  if (p.norm != DIT_ATTN_NORM_RMS_PER_HEAD && p.norm != DIT_ATTN_NORM_LAYER_ACROSS_HEADS)
+    return DIT_ATTN_ERR_UNSUPPORTED;
+  if ((has_q && H < 1) || H_kv < 1) return DIT_ATTN_ERR_SHAPE;
+  const int32_t Hq = has_q ? H : 0;
+  if (B > 65535) return DIT_ATTN_ERR_UNSUPPORTED;
+  const int chunk = dtype == DIT_ATTN_BF16 ? 8 : 4;
+  if (D < 8 || D > kMaxDim || D % chunk != 0) return DIT_ATTN_ERR_UNSUPPORTED;
+  if (p.norm == DIT_ATTN_NORM_LAYER_ACROSS_HEADS && (int64_t)(Hq + H_kv) * (D / chunk) > dit::kLayerNormMaxItems)
+    return DIT_ATTN_ERR_UNSUPPORTED;
+  dit::QkNormRopeArgs a{};
+  const int rs = rope_frequencies(D, n_axes, axes_dims, p.rope_theta, p.rope_linear_factor, p.rope_ntk_factor,
+                                  a.omega, a.pair_axis);
+  if (rs != DIT_ATTN_OK) return rs;
+  if (!(p.eps >= 0.f) || !std::isfinite(p.eps) || !std::isfinite(p.q_scale) || p.q_scale == 0.f)
     return DIT_ATTN_ERR_SHAPE;
-  if (!strides_ok(q_strides) || !strides_ok(k_strides) || !strides_ok(qo_strides) || !strides_ok(ko_strides))
+  if ((has_q && (!strides_ok(q_strides) || !strides_ok(qo_strides))) || !strides_ok(k_strides) ||
+      !strides_ok(ko_strides))
     return DIT_ATTN_ERR_SHAPE;
   const int es = elem_size(dtype);
-  if (!rows_aligned(q, q_strides, es) || !rows_aligned(k, k_strides, es) || !rows_aligned(q_out, qo_strides, es) ||
-      !rows_aligned(k_out, ko_strides, es) || (p.q_weight && !aligned16(p.q_weight)) ||
-      (p.k_weight && !aligned16(p.k_weight)) || (p.q_bias && !aligned16(p.q_bias)) ||
-      (p.k_bias && !aligned16(p.k_bias)))
+  if ((has_q && (!rows_aligned(q, q_strides, es) || !rows_aligned(q_out, qo_strides, es))) ||
+      !rows_aligned(k, k_strides, es) || !rows_aligned(k_out, ko_strides, es) ||
+      (p.q_weight && !aligned16(p.q_weight)) || (p.k_weight && !aligned16(p.k_weight)) ||
+      (p.q_bias && !aligned16(p.q_bias)) || (p.k_bias && !aligned16(p.k_bias)))
     return DIT_ATTN_ERR_ALIGN;
 
-  dit::QkNormRopeArgs a{};
   a.q = q;
   a.k = k;
   a.qo = q_out;
@@ -167,30 +192,18 @@ static int qknorm_rope_common(const void* q, const void* k, void* q_out, void* k
   }
   a.pos = pos_ids;
   for (int i = 0; i < 3; ++i) {
-    a.qs[i] = q_strides[i];
+    a.qs[i] = has_q ? q_strides[i] : 0;
     a.ks[i] = k_strides[i];
-    a.qos[i] = qo_strides[i];
+    a.qos[i] = has_q ? qo_strides[i] : 0;
     a.kos[i] = ko_strides[i];
   }
   a.B = B;
   a.S = S;
-  a.H = H;
+  a.H = Hq;
   a.Hk = H_kv;
   a.D = D;
   a.eps = p.eps;
   a.q_scale = p.q_scale;
-  // Pair j of axis a turns by (pos / linear) * (theta * ntk)^(-2j/d_a): both
-  // factors fold into the pair's frequency.
-  const double base = (double)p.rope_theta * (double)p.rope_ntk_factor;
-  const double lin = (double)p.rope_linear_factor;
-  int pr = 0;
-  for (int ax = 0; ax < n_axes; ++ax) {
-    const int da = axes_dims[ax];
-    for (int j = 0; j < da / 2; ++j, ++pr) {
-      a.omega[pr] = std::pow(base, -2.0 * j / da) / lin;
-      a.pair_axis[pr] = ax;
-    }
-  }
   hipError_t e = dit::launch_qknorm_rope(a, dtype, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? DIT_ATTN_OK : DIT_ATTN_ERR_HIP;
 }
@@ -241,11 +254,20 @@ int dit_attn_time_aware_rope_factors(float t, float watershed, float scaling_fac
   return DIT_ATTN_OK;
 }
 
+// Fused Q norm for attention_common (NULL: Q is already normed and rotated).
+struct QNormArgs {
+  const void* q_weight;
+  const int32_t* pos;  // [S_new][3]
+  float eps, q_scale;
+  const double* omega;       // [kMaxPairs], turns per position
+  const int32_t* pair_axis;  // [kMaxPairs]
+};
+
 static int attention_common(const void* q, const void* kc, const void* vc, const void* kn, const void* vn, void* o,
                             float* lse, int32_t B, int32_t P, int32_t S_new, int32_t H, int32_t H_kv, int32_t D,
                             const int64_t* const st[6], int32_t mask_mode, const dit_attn_token_meta* meta,
                             const uint64_t* key_valid, int64_t key_valid_stride, float softmax_scale,
-                            int32_t dtype, void* stream) {
+                            int32_t dtype, void* stream, const QNormArgs* qn = nullptr) {
   if (dtype != DIT_ATTN_BF16 && dtype != DIT_ATTN_F32) return DIT_ATTN_ERR_UNSUPPORTED;
   if (mask_mode != DIT_ATTN_MASK_FULL && mask_mode != DIT_ATTN_MASK_BLOCK_CAUSAL) return DIT_ATTN_ERR_UNSUPPORTED;
   if (B < 0 || P < 0 || S_new < 0 || H < 1 || H_kv < 1 || H % H_kv != 0) return DIT_ATTN_ERR_SHAPE;
@@ -304,6 +326,18 @@ static int attention_common(const void* q, const void* kc, const void* vc, const
   a.Snew = S_new;
   a.Sk = P + S_new;
   a.scale = (softmax_scale > 0.f && std::isfinite(softmax_scale)) ? softmax_scale : (float)(1.0 / std::sqrt((double)D));
+  if (qn != nullptr) {
+    // The scale (and log2 e) go into Q with its norm; the kernel then
+    // exponentiates its MFMA output directly (scale argument ln 2).
+    a.wq = qn->q_weight;
+    a.qpos = qn->pos;
+    a.eps = qn->eps;
+    a.q_scale = (float)((double)a.scale * 1.4426950408889634 * (double)qn->q_scale);
+    // Each pair's frequency under its own axis, 0 under the others.
+    for (int i = 0; i < dit::kMaxPairs; ++i)
+      for (int ax = 0; ax < 3; ++ax) a.omega_axis[ax][i] = qn->pair_axis[i] == ax ? qn->omega[i] : 0.0;
+    a.scale = 0.6931471805599453f;
+  }
   hipError_t e = dit::launch_attention(a, dtype, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? DIT_ATTN_OK : DIT_ATTN_ERR_HIP;
 }
@@ -356,6 +390,36 @@ int dit_attn_forward_cached_padded(const void* q_new, const void* k_cache, const
   const int64_t* st[6] = {strides[0], strides[1], strides[2], strides[3], strides[4], strides[5]};
   return attention_common(q_new, k_cache, v_cache, k_new, v_new, o, lse, B, P, S_new, H, H_kv, D, st, mask_mode,
                           meta, key_valid, key_valid_stride, softmax_scale, dtype, stream);
+}
+
+int dit_attn_forward_cached_qnorm(const void* q_new_raw, const void* k_cache, const void* v_cache, const void* k_new,
+                                  const void* v_new, void* o, float* lse, int32_t B, int32_t P, int32_t S_new,
+                                  int32_t H, int32_t H_kv, int32_t D, const int64_t strides[6][3], int32_t mask_mode,
+                                  const dit_attn_token_meta* meta, const uint64_t* key_valid,
+                                  int64_t key_valid_stride, const int32_t* pos_ids, int32_t n_axes,
+                                  const int32_t* axes_dims, const dit_attn_norm_rope_params* params,
+                                  float softmax_scale, int32_t dtype, void* stream) {
+  if (B < 0 || P < 0 || S_new < 0) return DIT_ATTN_ERR_SHAPE;
+  if (B == 0 || S_new == 0) return DIT_ATTN_OK;  // nothing to do; no pointer is read
+  if (!q_new_raw || !k_new || !v_new || !o || !strides || !pos_ids || !params) return DIT_ATTN_ERR_NULL;
+  if (P > 0 && (!k_cache || !v_cache)) return DIT_ATTN_ERR_NULL;
+  if (dtype != DIT_ATTN_BF16) return DIT_ATTN_ERR_UNSUPPORTED;  // the fused form is bf16 only
+  if (params->norm != DIT_ATTN_NORM_RMS_PER_HEAD) return DIT_ATTN_ERR_UNSUPPORTED;
+  if (D < 8 || D > kMaxDim) return DIT_ATTN_ERR_UNSUPPORTED;
+  double omega[dit::kMaxPairs] = {};
+  int32_t pair_axis[dit::kMaxPairs] = {};
+  const int rs = rope_frequencies(D, n_axes, axes_dims, params->rope_theta, params->rope_linear_factor,
+                                  params->rope_ntk_factor, omega, pair_axis);
+  if (rs != DIT_ATTN_OK) return rs;
+  if (!(params->eps >= 0.f) || !std::isfinite(params->eps) || !std::isfinite(params->q_scale) ||
+      params->q_scale == 0.f)
+    return DIT_ATTN_ERR_SHAPE;
+  if (params->q_weight && !aligned16(params->q_weight)) return DIT_ATTN_ERR_ALIGN;
+  if (reinterpret_cast<uintptr_t>(pos_ids) & 3u) return DIT_ATTN_ERR_ALIGN;
+  const int64_t* st[6] = {strides[0], strides[1], strides[2], strides[3], strides[4], strides[5]};
+  QNormArgs qn{params->q_weight, pos_ids, params->eps, params->q_scale, omega, pair_axis};
+  return attention_common(q_new_raw, k_cache, v_cache, k_new, v_new, o, lse, B, P, S_new, H, H_kv, D, st, mask_mode,
+                          meta, key_valid, key_valid_stride, softmax_scale, dtype, stream, &qn);
 }
 
 int dit_attn_cfg_norm_rescale(const void* cond, const void* uncond, void* out, int64_t rows, int32_t channels,

@@ -124,7 +124,11 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, char* dst, in
 // ALIGNED: the cache length P is a multiple of the key tile, so no tile mixes
 // cached and new keys and every tile load comes from one source.
 // PADDED: a.key_bits marks the valid keys of each sample.
-template <int DP, int NW, bool UNIT, bool ALIGNED, bool PADDED>
+// QNORM: a.q holds raw Q; the prologue applies the per-head RMSNorm, the
+// weight, the rotary embedding (phases from a.qpos and a.omega) and a.q_scale,
+// and rounds once, as the norm kernel would have, so Q' never goes through
+// memory.
+template <int DP, int NW, bool UNIT, bool ALIGNED, bool PADDED, bool QNORM>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   static_assert(DP % 32 == 0 && DP <= 128, "padded head dim");
   constexpr int KSTEPS = DP / 16;  // QK^T contraction steps
@@ -187,6 +191,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
 
   // Q^T operand: lane holds query (lane & 31), channels 16*ks + 8*g .. +7.
   bf16x8 qreg[KSTEPS];
+  constexpr int QN = QNORM ? KSTEPS : 1;
+  u32x4 qn_w[QN];                 // fused Q norm: weight chunk per Q chunk
+  int qn_p0 = 0, qn_p1 = 0, qn_p2 = 0;  // fused Q norm: the row's positions
   {
     const __bf16* qp = reinterpret_cast<const __bf16*>(a.q) + b * a.qs[0] + (int64_t)qclamp * a.qs[1] + h * a.qs[2];
 #pragma unroll
@@ -197,7 +204,86 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
       else
         qreg[ks] = bf16x8{};
     }
+    if constexpr (QNORM) {
+      // The weight chunks of this lane's channels and the row's positions,
+      // read with Q; the norm itself runs once the first key/value tiles are
+      // in flight (qnorm_apply), so these loads overlap theirs.
+      const __bf16* wp = reinterpret_cast<const __bf16*>(a.wq);
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        const int d0 = 16 * ks + 8 * g;
+        qn_w[ks] = u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};  // bf16 pairs of 1.0
+        if (wp != nullptr && d0 < a.D && row_ok) qn_w[ks] = *reinterpret_cast<const u32x4*>(wp + d0);
+      }
+      const int32_t* pp = a.qpos + 3 * (int64_t)qclamp;
+      qn_p0 = pp[0];
+      qn_p1 = pp[1];
+      qn_p2 = pp[2];
+    }
   }
+  // Q's RMSNorm over the D channels (the row is split between this lane and
+  // the lane 32 apart, the other k-group: one exchange completes the sum of
+  // squares), the weight, the rotation and q_scale, rounded once to bf16.
+  // Pair p = 8 ks + 4 g + i of the row turns by pos[axis_p] * omega_p turns,
+  // formed in double (as a sum over the three axes with the other axes'
+  // frequencies 0, so without a per-pair choice of axis) and evaluated as the
+  // norm kernel evaluates it, so Q and K turn by the same angles.
+  auto qnorm_apply = [&]() __attribute__((always_inline)) {
+    if constexpr (QNORM) {
+      // Nothing moves above this point: the first tiles' loads are issued
+      // before the wait for Q, which then counts only the older loads.
+      __builtin_amdgcn_sched_barrier(0);
+      float ss = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        const u32x4 w = __builtin_bit_cast(u32x4, qreg[ks]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x0 = bf16_lo(w[i]), x1 = bf16_hi(w[i]);
+          ss = fmaf(x0, x0, ss);
+          ss = fmaf(x1, x1, ss);
+        }
+      }
+      ss += __shfl_xor(ss, 32, 64);
+      const float inv = 1.0f / sqrtf(ss / (float)a.D + a.eps) * a.q_scale;
+      const double pd0 = qn_p0, pd1 = qn_p1, pd2 = qn_p2;
+      // The frequencies are read through the kernel-argument segment (the
+      // argument struct sits at its start) where they are used, so that one
+      // chunk's worth is live at a time instead of all of them from entry.
+      using const_f64 = const __attribute__((address_space(4))) double;
+      const_f64* om = (const_f64*)((const_u8*)__builtin_amdgcn_kernarg_segment_ptr() + offsetof(AttnArgs, omega_axis));
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        const int d0 = 16 * ks + 8 * g;
+        const u32x4 w = __builtin_bit_cast(u32x4, qreg[ks]);
+        u32x4 o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          // This chunk's pair i is pair j0 in k-group 0 and j0 + 4 in k-group
+          // 1.  Both phases are formed from wave-uniform frequencies (scalar
+          // loads) and the lane keeps its own: selecting a frequency per lane
+          // would turn its load into a per-lane one.
+          const int j0 = 8 * ks + i;
+          constexpr int M = kMaxPairs;
+          const double t0 = fma(pd2, om[2 * M + j0], fma(pd1, om[M + j0], pd0 * om[j0]));
+          const double t1 = fma(pd2, om[2 * M + j0 + 4], fma(pd1, om[M + j0 + 4], pd0 * om[j0 + 4]));
+          float sn, cs;
+          sincos_turns(g ? t1 : t0, sn, cs);
+          const float y0 = bf16_lo(w[i]) * inv * bf16_lo(qn_w[ks][i]);
+          const float y1 = bf16_hi(w[i]) * inv * bf16_hi(qn_w[ks][i]);
+          o[i] = pack_bf16x2(y0 * cs - y1 * sn, y0 * sn + y1 * cs);
+        }
+        // Channels past D and rows past the end keep their zeros.
+        const bool keep = d0 < a.D && row_ok;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = keep ? o[i] : w[i];
+        qreg[ks] = __builtin_bit_cast(bf16x8, o);
+        // One chunk's frequencies live at a time: hoisting every scalar load
+        // to the top would hold 384 SGPRs and spill.
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
 
   // Key tiles this work-group visits (the largest bound of its waves).  Bare
   // barrier: only the s_lim stores must have landed, not the Q loads.
@@ -510,6 +596,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
     issue(0, sK0, true);
     issue(1, sK1, true);
     issue(0, sV0, false);
+    qnorm_apply();
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -565,6 +652,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
     issue(t0, sK0, true);
     issue(tb, sK1, true);
     issue(t0, sV0, false);
+    qnorm_apply();
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -723,10 +811,21 @@ constexpr int kWaves = 4;
 template <int DP, bool UNIT, bool ALIGNED>
 void launch_bf16_variant(const AttnArgs& a, dim3 grid, hipStream_t stream) {
   const dim3 block(kWaves * 64);
+  if constexpr (UNIT) {  // the fused Q norm always folds the scale into Q
+    if (a.qpos != nullptr) {
+      if (a.key_bits != nullptr)
+        hipLaunchKernelGGL((attn_fwd_bf16_kernel<DP, kWaves, true, ALIGNED, true, true>), grid, block, 0, stream,
+                           a);
+      else
+        hipLaunchKernelGGL((attn_fwd_bf16_kernel<DP, kWaves, true, ALIGNED, false, true>), grid, block, 0, stream,
+                           a);
+      return;
+    }
+  }
   if (a.key_bits != nullptr)
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<DP, kWaves, UNIT, ALIGNED, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<DP, kWaves, UNIT, ALIGNED, true, false>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<DP, kWaves, UNIT, ALIGNED, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<DP, kWaves, UNIT, ALIGNED, false, false>), grid, block, 0, stream, a);
 }
 
 template <int DP>

@@ -52,7 +52,7 @@ struct QkNormRopeArgs {
   int32_t B, S, H, Hk, D;
   float eps;
   float q_scale;                 // extra factor on Q outputs
-  double omega[kMaxPairs];       // frequency of channel pair p
+  double omega[kMaxPairs];       // frequency of channel pair p, in turns per position
   int32_t pair_axis[kMaxPairs];  // axis that owns pair p
 };
 
@@ -78,6 +78,16 @@ struct AttnArgs {
   int64_t qs[3], kcs[3], vcs[3], kns[3], vns[3], os[3];
   int32_t B, H, Hk, D, P, Snew, Sk;
   float scale;               // softmax scale
+  // Fused Q norm, active when qpos is set (q then holds raw Q): per-head
+  // RMSNorm with weight wq (nullable: unit) and eps, the rotary embedding of
+  // each query's token and the factor q_scale, rounded once to bf16.  Pair p
+  // turns by sum_a qpos[3 i + a] * omega_axis[a][p] turns: omega_axis holds
+  // the pair's frequency under the axis that owns it and 0 under the others,
+  // so the sum is exactly the norm kernel's pos * omega.
+  const void* wq;
+  const int32_t* qpos;       // [Snew][3] positions of the query tokens
+  float eps, q_scale;
+  double omega_axis[3][kMaxPairs];
 };
 
 hipError_t launch_attention(const AttnArgs& a, int dtype, hipStream_t stream);

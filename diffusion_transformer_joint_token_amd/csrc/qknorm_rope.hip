@@ -9,8 +9,9 @@
 //
 // HBM-bound: each element is read once and written once.  One work-group
 // handles one token (b, s) for all H query heads and H_kv key heads, so the
-// token's rotary phases (one cos/sin per channel pair) are computed once, in
-// double precision before the final fp32 sincos, and shared by every head.
+// token's rotary phases (one cos/sin per channel pair) are computed once
+// (whole turns removed in double precision, then sin/cos in fp32: see
+// sincos_turns) and shared by every head.
 // A group of LPH lanes owns one head; each lane holds a 16-byte chunk of it
 // (8 bf16 or 4 fp32), so loads and stores are full 16-byte vectors and a
 // head's sum of squares is a butterfly over LPH lanes.  When a head's chunk
@@ -124,15 +125,12 @@ __global__ __launch_bounds__(kThreads) void qknorm_rope_kernel(QkNormRopeArgs a)
       }
     }
     if (first) {
-      // Rotary phases of this token, one per channel pair: phase = pos * omega
-      // in double, reduced to [-pi, pi] before the fp32 sincos.
+      // Rotary phases of this token, one per channel pair: pos * omega turns,
+      // formed in double.
       if (tid < D / 2) {
         const int ax = a.pair_axis[tid];
-        const double phase = (double)a.pos[3 * s + ax] * a.omega[tid];
-        const double turns = rint(phase * 0.15915494309189535);  // 1 / (2 pi)
-        const float red = (float)fma(-turns, 6.283185307179586, phase);
         float sn, cs;
-        sincosf(red, &sn, &cs);
+        sincos_turns((double)a.pos[3 * s + ax] * a.omega[tid], sn, cs);
         s_cs[tid] = make_float2(cs, sn);
       }
       __syncthreads();
@@ -223,11 +221,8 @@ __global__ __launch_bounds__(kThreads) void qknorm_rope_flat_kernel(QkNormRopeAr
   for (int p = tid; p < tpw * (D / 2); p += kThreads) {
     const int tt = p / (D / 2), j = p - tt * (D / 2);
     const int s = min(s0 + tt, a.S - 1);
-    const double phase = (double)a.pos[3 * s + a.pair_axis[j]] * a.omega[j];
-    const double turns = rint(phase * 0.15915494309189535);  // 1 / (2 pi)
-    const float red = (float)fma(-turns, 6.283185307179586, phase);
     float sn, cs;
-    sincosf(red, &sn, &cs);
+    sincos_turns((double)a.pos[3 * s + a.pair_axis[j]] * a.omega[j], sn, cs);
     s_cs[tt][j] = make_float2(cs, sn);
   }
   // Partial sums of squares.
@@ -334,11 +329,8 @@ __global__ __launch_bounds__(kThreads) void qk_layernorm_rope_kernel(QkNormRopeA
   }
   if (tid < D / 2) {  // rotary phases of this token, as in the per-head kernel
     const int ax = a.pair_axis[tid];
-    const double phase = (double)a.pos[3 * s + ax] * a.omega[tid];
-    const double turns = rint(phase * 0.15915494309189535);  // 1 / (2 pi)
-    const float red = (float)fma(-turns, 6.283185307179586, phase);
     float sn, cs;
-    sincosf(red, &sn, &cs);
+    sincos_turns((double)a.pos[3 * s + ax] * a.omega[tid], sn, cs);
     s_cs[tid] = make_float2(cs, sn);
   }
 

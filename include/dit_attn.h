@@ -209,6 +209,8 @@ typedef struct {
  * statistics for Q (over H * D channels) and K (over H_kv * D channels), in
  * fp32, reduced in a fixed order.  Limits: (H + H_kv) * D / 8 (bf16) or / 4
  * (f32) <= 2048 for the LayerNorm; otherwise as dit_attn_qknorm_rope.
+ * q and q_out may both be NULL (with their strides): K only, H ignored -- the
+ * form that goes with dit_attn_forward_cached_qnorm, which norms Q itself.
  * params is a host pointer (NULL -> DIT_ATTN_ERR_NULL). */
 int dit_attn_qknorm_rope_ex(const void *q, const void *k, void *q_out, void *k_out,
                             int32_t B, int32_t S, int32_t H, int32_t H_kv, int32_t D,
@@ -291,6 +293,40 @@ int dit_attn_forward_cached_padded(const void *q_new, const void *k_cache, const
                                    const dit_attn_token_meta *meta, const uint64_t *key_valid,
                                    int64_t key_valid_stride, float softmax_scale, int32_t dtype,
                                    void *stream);
+
+/* Attention (plain, cached or padded) on raw Q: the per-head RMSNorm of Q,
+ * its rotary embedding and the softmax scale are applied inside the attention
+ * kernel as each work-group loads its query rows, so the normed Q never goes
+ * through memory (NucleusMoE-Image pipeline article, section 6.3: qk_norm,
+ * then the rotary embedding, then attention).  K must already be normed and
+ * rotated: dit_attn_qknorm_rope_ex with q = q_out = NULL does K alone.
+ * Per query row x of token i:
+ *   y = x / sqrt(mean_D x^2 + eps) * q_weight, rotated as dit_attn_qknorm_rope_ex
+ *   rotates (pair j of axis a by pos_ids[i][a] / rope_linear_factor *
+ *   (rope_theta * rope_ntk_factor)^(-2j/d_a), the same angles bit for bit),
+ *   times q_scale * softmax_scale * log2(e), rounded once to bf16
+ * -- the Q' that dit_attn_qknorm_rope_ex with that q_scale produces, up to
+ * the summation order of mean_D x^2 -- then the attention of
+ * dit_attn_forward_cached_padded with scale ln 2.
+ *   q_new_raw  device [B, S_new, H, D] raw Q (stride strides[0]).
+ *   pos_ids    device int32 [S_new][3], 4-byte aligned: positions of the query
+ *              tokens (the metadata's pos_ids + 3 * P).
+ *   n_axes, axes_dims  as dit_attn_qknorm_rope.
+ *   params     host: norm must be DIT_ATTN_NORM_RMS_PER_HEAD
+ *              (DIT_ATTN_ERR_UNSUPPORTED otherwise); q_weight (device bf16
+ *              [D] or NULL), eps, rope_theta, the two rotary factors and
+ *              q_scale are used; the k_ and bias fields are ignored.
+ *   key_valid  as dit_attn_forward_cached_padded, or NULL (no padding).
+ *   P == 0 is the plain forward; other arguments as dit_attn_forward_cached.
+ * bf16 only (DIT_ATTN_ERR_UNSUPPORTED otherwise). */
+int dit_attn_forward_cached_qnorm(const void *q_new_raw, const void *k_cache, const void *v_cache,
+                                  const void *k_new, const void *v_new, void *o, float *lse,
+                                  int32_t B, int32_t P, int32_t S_new, int32_t H, int32_t H_kv,
+                                  int32_t D, const int64_t strides[6][3], int32_t mask_mode,
+                                  const dit_attn_token_meta *meta, const uint64_t *key_valid,
+                                  int64_t key_valid_stride, const int32_t *pos_ids, int32_t n_axes,
+                                  const int32_t *axes_dims, const dit_attn_norm_rope_params *params,
+                                  float softmax_scale, int32_t dtype, void *stream);
 
 /* Classifier-free guidance with norm rescaling (NucleusMoE-Image pipeline
  * article, section 4.3), row by row (a row = one token's C channels):

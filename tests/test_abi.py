@@ -203,6 +203,68 @@ def test_qknorm_rope_ex_argument_errors():
     assert call(prm(), B=0, q=None) == _lib.OK
 
 
+def test_fused_qnorm_attention_argument_errors():
+    """dit_attn_forward_cached_qnorm: bf16 and the per-head RMSNorm only, needs
+    the positions and the options, checks the rotary axes and factors, eps and
+    the alignment of the weight, then the checks of the cached / padded forms."""
+    from diffusion_transformer_joint_token_amd import _lib
+    f = _lib.lib.dit_attn_forward_cached_qnorm
+    st6 = (_lib.Strides3 * 6)(*[_s3(4096 * 4096, 4096, 128)] * 6)
+
+    def prm(**kw):
+        p = _lib.NormRopeParams(0, None, None, None, None, 1e-6, 1e4, 1.0, 1.0, 1.0)
+        for k, v in kw.items():
+            setattr(p, k, v)
+        return p
+
+    def call(q=FAKE, kc=FAKE, P=16, kb=None, words=0, pos=FAKE2, axes=(16, 56, 56), params=None, dtype=0, B=1,
+             S=100, D=128):
+        ax = (ctypes.c_int32 * len(axes))(*axes)
+        p = prm() if params is None else params
+        return f(q, kc, FAKE, FAKE, FAKE, FAKE2, None, B, P, S, 32, 32, D, st6, 1, ctypes.byref(_meta(P + S)), kb,
+                 words, pos, len(axes), ax, ctypes.byref(p) if params != "null" else None, 0.0, dtype, None)
+    assert call(pos=None) == _lib.ERR_NULL
+    assert call(params="null") == _lib.ERR_NULL
+    assert call(q=None) == _lib.ERR_NULL
+    assert call(kc=None) == _lib.ERR_NULL               # P > 0 needs the cache
+    assert call(dtype=1) == _lib.ERR_UNSUPPORTED        # fused form is bf16 only
+    assert call(params=prm(norm=1)) == _lib.ERR_UNSUPPORTED  # per-head RMSNorm only
+    assert call(D=136, axes=(16, 56, 64)) == _lib.ERR_UNSUPPORTED
+    assert call(axes=(16, 56, 58)) == _lib.ERR_SHAPE    # axes must sum to D
+    assert call(axes=(17, 55, 56)) == _lib.ERR_SHAPE    # and be even
+    assert call(params=prm(rope_ntk_factor=0.0)) == _lib.ERR_SHAPE
+    assert call(params=prm(rope_linear_factor=float("inf"))) == _lib.ERR_SHAPE
+    assert call(params=prm(rope_theta=-1.0)) == _lib.ERR_SHAPE
+    assert call(params=prm(eps=-1.0)) == _lib.ERR_SHAPE
+    assert call(params=prm(eps=float("nan"))) == _lib.ERR_SHAPE
+    assert call(params=prm(q_scale=0.0)) == _lib.ERR_SHAPE
+    assert call(params=prm(q_weight=FAKE + 2)) == _lib.ERR_ALIGN
+    assert call(pos=FAKE2 + 2) == _lib.ERR_ALIGN
+    assert call(kb=FAKE2, words=1) == _lib.ERR_SHAPE    # 116 logical keys need 2 words
+    assert call(B=0, q=None, pos=None) == _lib.OK       # empty: nothing read
+    assert call(S=0, q=None) == _lib.OK
+
+
+def test_qknorm_rope_k_only_argument_errors():
+    """q and q_out both NULL is the K-only form (H ignored); one of them alone
+    is an error."""
+    from diffusion_transformer_joint_token_amd import _lib
+    f = _lib.lib.dit_attn_qknorm_rope_ex
+    st = _s3(4096 * 8 * 128, 8 * 128, 128)
+    axes = (ctypes.c_int32 * 3)(32, 48, 48)
+
+    def call(q=None, qo=None, H=0, Hk=8, D=128, norm=0):
+        p = _lib.NormRopeParams(norm, None, None, None, None, 1e-6, 1e4, 1.0, 1.0, 1.0)
+        return f(q, FAKE, qo, FAKE2, 1, 4096, H, Hk, D, st, st, st, st, FAKE, 3, axes, ctypes.byref(p), 0, None)
+    assert call(qo=FAKE2, H=32) == _lib.ERR_NULL        # q_out without q
+    assert call(q=FAKE, H=32) == _lib.ERR_NULL          # q without q_out
+    assert call(q=FAKE, qo=FAKE2, H=0) == _lib.ERR_SHAPE  # with Q, H must be >= 1
+    assert call(Hk=0) == _lib.ERR_SHAPE
+    assert call(D=136) == _lib.ERR_UNSUPPORTED
+    # the LayerNorm item limit counts Q's heads only when Q is there
+    assert call(q=FAKE, qo=FAKE2, H=256, Hk=8, norm=1) == _lib.ERR_UNSUPPORTED  # (256 + 8) * 16 > 2048
+
+
 def test_time_aware_factors_host_helper():
     """The C helper against the oracle's switch (the product's only host-side
     arithmetic of the method), and its argument errors."""
