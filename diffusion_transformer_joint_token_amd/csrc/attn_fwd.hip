@@ -130,10 +130,13 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, char* dst, in
 // memory.
 template <int DP, int NW, bool UNIT, bool ALIGNED, bool PADDED, bool QNORM>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
-  static_assert(DP % 32 == 0 && DP <= 128, "padded head dim");
-  constexpr int KSTEPS = DP / 16;  // QK^T contraction steps
-  constexpr int MBLK = DP / 32;    // 32-channel blocks of O^T
-  constexpr int CHUNKS = DP / 8;   // 16-byte chunks per key row actually used
+  // DP: head dim padded to a multiple of 16 for QK^T (80 for head dim 72: five
+  // contraction steps, not six); O^T runs in 32-channel blocks, so its last
+  // block may reach past DP, where the tiles hold zeros.
+  static_assert(DP % 16 == 0 && DP >= 32 && DP <= 128, "padded head dim");
+  constexpr int KSTEPS = DP / 16;         // QK^T contraction steps
+  constexpr int MBLK = (DP + 31) / 32;    // 32-channel blocks of O^T
+  constexpr int CHUNKS = DP / 8;          // 16-byte chunks per key row actually used
   constexpr int LOADS = (kTileN * 16) / (NW * 64);  // LDS-load instructions per wave per tile
 
   // Two K stages and two V stages, each a distinct LDS object, so the compiler
@@ -860,6 +863,8 @@ hipError_t launch_f32(const AttnArgs& a, hipStream_t stream) {
 hipError_t launch_attention(const AttnArgs& a, int dtype, hipStream_t stream) {
   const int dp = (a.D + 31) / 32 * 32;
   if (dtype == 0) {
+    // Head dims 65..80 (Lumina-Next's 72) take five QK^T steps instead of six.
+    if (a.D > 64 && a.D <= 80) return launch_bf16<80>(a, stream);
     switch (dp) {
       case 32: return launch_bf16<32>(a, stream);
       case 64: return launch_bf16<64>(a, stream);
