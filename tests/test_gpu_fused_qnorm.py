@@ -68,6 +68,7 @@ FUSED_CASES = [
      False, None),
     (2, 4, 2, 128, (("T", 100), ("I", 1, 6, 10), ("T", 37), ("I", 1, 4, 8)), (32, 48, 48), "full", 0, True, None),
     (1, 6, 3, 72, (("I", 1, 14, 22),), (24, 24, 24), "full", 0, False, None),
+    (2, 4, 2, 80, (("T", 90), ("I", 1, 10, 12)), (16, 32, 32), "block_causal", 45, False, "random"),
     (2, 2, 1, 16, (("T", 5), ("I", 1, 2, 4), ("T", 70), ("I", 1, 8, 8)), (4, 6, 6), "block_causal", 0, False, None),
     (1, 4, 4, 64, (("T", 256), ("I", 1, 8, 8), ("I", 1, 8, 8), ("T", 30), ("I", 1, 10, 16)), (16, 24, 24),
      "block_causal", 0, False, None),

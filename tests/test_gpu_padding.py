@@ -131,6 +131,7 @@ PAD_CASES = [
     (2, 4, 2, 128, (("T", 100), ("I", 1, 6, 10), ("T", 37), ("I", 1, 4, 8)), "block_causal", "bf16", 0, "right"),
     (2, 4, 2, 128, (("T", 100), ("I", 1, 6, 10), ("T", 37), ("I", 1, 4, 8)), "full", "bf16", 0, "random"),
     (3, 6, 3, 72, (("T", 150), ("I", 1, 14, 22)), "full", "bf16", 0, "random"),
+    (2, 4, 4, 80, (("T", 130), ("I", 1, 10, 12)), "block_causal", "bf16", 64, "right"),
     (2, 2, 1, 16, (("T", 5), ("I", 1, 2, 4), ("T", 70), ("I", 1, 8, 8)), "block_causal", "bf16", 0, "random"),
     (2, 4, 4, 64, (("T", 256), ("I", 1, 8, 8), ("T", 30), ("I", 1, 10, 16)), "block_causal", "bf16", 0, "lead"),
     (2, 4, 2, 128, (("T", 130), ("I", 1, 4, 8), ("I", 1, 10, 20)), "block_causal", "bf16", 162, "random"),

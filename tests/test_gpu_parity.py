@@ -250,6 +250,7 @@ ATT_CASES = [
     (2, 4, 2, 128, (("T", 100), ("I", 1, 6, 10), ("T", 37), ("I", 1, 4, 8)), "block_causal", "bf16", 0),
     (2, 4, 2, 128, (("T", 100), ("I", 1, 6, 10), ("T", 37), ("I", 1, 4, 8)), "full", "bf16", 0),
     (1, 6, 3, 72, (("I", 1, 14, 22),), "full", "bf16", 0),
+    (2, 4, 2, 80, (("T", 50), ("I", 1, 6, 10), ("I", 1, 8, 8)), "block_causal", "bf16", 70),
     (1, 3, 1, 8, (("I", 1, 4, 4),), "full", "bf16", 0),
     (2, 2, 1, 16, (("T", 5), ("I", 1, 2, 4), ("T", 70), ("I", 1, 8, 8)), "block_causal", "bf16", 0),
     (1, 4, 4, 64, (("T", 256), ("I", 1, 8, 8), ("I", 1, 8, 8), ("T", 30), ("I", 1, 10, 16)), "block_causal",
