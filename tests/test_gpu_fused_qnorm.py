@@ -263,3 +263,37 @@ def test_fused_padded_workload_sampled(dit):
     idx = torch.from_numpy(rows).cuda()
     assert_parity(to_host(o[:, idx]), ro, "bf16", "O")
     _check_lse(lse[:, :, idx].cpu().double().numpy(), rl)
+
+
+def test_fused_strided_views_and_in_place_k(dit):
+    """Q, K and V as views of one projection buffer (heads interleaved, a
+    spare head between them), K normed in place, O written into a wider
+    buffer: bit-identical to the same call on contiguous copies, and the
+    spare head and the columns around O untouched."""
+    B, H, Hk, D = 2, 4, 2, 128
+    w = wl.small_workload("v", B, H, Hk, D, (("T", 77), ("I", 1, 8, 12), ("I", 1, 6, 10)), (16, 56, 56), seed=9)
+    d = wl.draw(w)
+    mask, shapes = wl.sequence_inputs(w)
+    m = dit.build_token_metadata(torch.from_numpy(mask).cuda(), shapes)
+    m.check()
+    q, k, v = (to_device(d.bits[n], "bf16") for n in ("q", "k", "v"))
+    wq, wk = to_device(d.bits["wq"], "bf16"), to_device(d.bits["wk"], "bf16")
+    S = w.n_new
+    qkv = torch.full((B, S, H + 2 * Hk + 1, D), 7.0, dtype=torch.bfloat16, device="cuda")
+    qkv[:, :, :H] = q
+    qkv[:, :, H:H + Hk] = k
+    qkv[:, :, H + Hk + 1:] = v  # spare head H + Hk stays 7
+    qv, kv, vv = qkv[:, :, :H], qkv[:, :, H:H + Hk], qkv[:, :, H + Hk + 1:]
+    wide = torch.full((B, S, H + 1, D), -3.0, dtype=torch.bfloat16, device="cuda")
+    ov = wide[:, :, 1:]
+    dit.dit_attn_qknorm_rope_ex(None, kv, m.pos_ids, w.axes, w.eps, k_weight=wk, k_out=kv)
+    dit.forward_cached_qnorm(qv, None, None, kv, vv, m.pos_ids, w.axes, w.eps, q_weight=wq, mask_mode=w.mask_mode,
+                             meta=m, out=ov)
+    _, kp = dit.dit_attn_qknorm_rope_ex(None, k, m.pos_ids, w.axes, w.eps, k_weight=wk)
+    o = dit.forward_cached_qnorm(q, None, None, kp, v, m.pos_ids, w.axes, w.eps, q_weight=wq, mask_mode=w.mask_mode,
+                                 meta=m)
+    torch.cuda.synchronize()
+    assert torch.equal(kv, kp)
+    assert torch.equal(ov, o)
+    assert torch.all(qkv[:, :, H + Hk] == 7.0) and torch.all(wide[:, :, 0] == -3.0)
+    assert torch.equal(qv, q) and torch.equal(vv, v)
