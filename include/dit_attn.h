@@ -160,6 +160,9 @@ int dit_attn_build_key_valid(const uint8_t *image_pad_mask, int32_t seq_len, con
  * q_scale = log2(e) * softmax_scale folds the attention's softmax scale into Q
  * with a single rounding (then call the attention with softmax_scale = ln 2).
  * V is not touched.  Arithmetic in fp32; outputs rounded to the dtype (RNE).
+ * Angles: pos * rope_theta^(-2j/d_a) / (2 pi) turns formed in double, whole
+ * turns removed exactly, the fraction rounded to fp32 and its sin and cos
+ * taken by the hardware instructions (absolute error <= 1.3e-7, measured).
  *   q, k           device [B, S, H | H_kv, D] in dtype, strides q_strides/k_strides.
  *   q_out, k_out   device outputs (may alias q, k exactly), strides qo_/ko_strides.
  *   q_weight, k_weight  device [D] in dtype, or NULL for unit weights.
