@@ -137,6 +137,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   constexpr int KSTEPS = DP / 16;         // QK^T contraction steps
   constexpr int MBLK = (DP + 31) / 32;    // 32-channel blocks of O^T
   constexpr int CHUNKS = DP / 8;          // 16-byte chunks per key row actually used
+  // When the O^T blocks reach past DP, V's logical chunk CHUNKS is set to
+  // (1, 0, ..., 0) in every V tile once it has landed (ones_col below), so
+  // O^T channel 8 * CHUNKS accumulates sum_k P[q, k]: the row sum comes out of
+  // the PV MFMAs, rescaled with O, instead of one dot product per pair of
+  // probabilities.
+  constexpr bool ONES_COL = 32 * MBLK > DP;
   constexpr int LOADS = (kTileN * 16) / (NW * 64);  // LDS-load instructions per wave per tile
 
   // Two K stages and two V stages, each a distinct LDS object, so the compiler
@@ -476,7 +482,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
         for (int j = 0; j < 4; ++j) {
           const float x0 = sacc[kb][8 * half + 2 * j], x1 = sacc[kb][8 * half + 2 * j + 1];
           w[j] = pack_bf16x2(__builtin_amdgcn_exp2f(UNIT ? x0 : x0 * c2), __builtin_amdgcn_exp2f(UNIT ? x1 : x1 * c2));
-          l_part = add_bf16_pair(w[j], l_part);
+          if constexpr (!ONES_COL) l_part = add_bf16_pair(w[j], l_part);
         }
         pop[kb][half] = __builtin_bit_cast(bf16x8, w);
       }
@@ -593,6 +599,29 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
+  // The ones column of a landed V tile.  Each wave writes it into the 16 rows
+  // its own loads filled (rows 4 wave + j + 16 i), after its wait for those
+  // loads and before the barrier that hands the tile to every wave: no other
+  // wave's loads touch those rows, and the load issues stay unconditional.
+  auto ones_col = [&](char* vt) __attribute__((always_inline)) {
+    if constexpr (ONES_COL) {
+      if ((lane & 15) < 4) {
+        const int row = 4 * wv + (lane >> 4) + kSlab * (lane & 3);
+        *reinterpret_cast<u32x4*>(vt + row * kRowBytes + ((CHUNKS ^ swz(row)) << 4)) =
+            u32x4{0x3f80u, 0u, 0u, 0u};  // bf16 1.0 in channel 8 * CHUNKS
+      }
+    }
+  };
+  // As wait_tile, for the barrier after which the V tile in vt is read.
+  auto wait_tile_v = [&](char* vt) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * LOADS, 0));
+    if constexpr (ONES_COL) {
+      ones_col(vt);
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+    }
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
 
   if constexpr (!PADDED) {
     // Prologue: K(0), K(1), V(0); S(0) once they land; then K(2).
@@ -601,6 +630,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
     issue(0, sV0, false);
     qnorm_apply();
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+    if constexpr (ONES_COL) {
+      ones_col(sV0);
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+    }
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     qk(sK0, sA);
@@ -616,14 +649,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
       wait_tile();  // K(t+1) in sK1; sV1 (V(t-1)) read by every wave
       issue(t + 1, sV1, false);
       phase1(t, t + 1, sK1, sA, sB);
-      wait_tile();  // V(t) in sV0; sK1 (K(t+1)) read by every wave
+      wait_tile_v(sV0);  // V(t) in sV0; sK1 (K(t+1)) read by every wave
       issue(t + 3, sK1, true);
       phase2(t, t + 1, sV0, sB, ~0ull);
       if (t + 1 >= n_tiles) break;
       wait_tile();  // K(t+2) in sK0; sV0 (V(t)) read by every wave
       issue(t + 2, sV0, false);
       phase1(t + 1, t + 2, sK0, sB, sA);
-      wait_tile();  // V(t+1) in sV1; sK0 (K(t+2)) read by every wave
+      wait_tile_v(sV1);  // V(t+1) in sV1; sK0 (K(t+2)) read by every wave
       issue(t + 4, sK0, true);
       phase2(t + 1, t + 2, sV1, sA, ~0ull);
     }
@@ -657,6 +690,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
     issue(t0, sV0, false);
     qnorm_apply();
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+    if constexpr (ONES_COL) {
+      ones_col(sV0);
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+    }
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     qk(sK0, sA);
@@ -672,7 +709,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
       issue(tb, sV1, false);
       phase1(ta, tb, sK1, sA, sB);
       uint64_t wd = tile_word(min(tc + 1, last_tile));
-      wait_tile();  // V(T(i)) in sV0
+      wait_tile_v(sV0);  // V(T(i)) in sV0
       int td = skip_empty(tc + 1, wd);  // T(i+3)
       issue(td, sK1, true);
       phase2(ta, tb, sV0, sB, wb);
@@ -683,7 +720,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
       issue(tb, sV0, false);
       phase1(ta, tb, sK0, sB, sA);
       wd = tile_word(min(tc + 1, last_tile));
-      wait_tile();  // V(T(i+1)) in sV1
+      wait_tile_v(sV1);  // V(T(i+1)) in sV1
       td = skip_empty(tc + 1, wd);
       issue(td, sK0, true);
       phase2(ta, tb, sV1, sA, wb);
@@ -697,7 +734,16 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
 
   // Normalise and store: lane holds query (lane & 31), channels
   // 32*mb + 8*(i/4) + 4*g + (i%4).
-  const float l_tot = sum_with_partner32(l_part);
+  float l_own = l_part;
+  if constexpr (ONES_COL) {
+    // Channel 8 * CHUNKS is element (c0 / 8) * 4 of the last O^T block in
+    // the k-group-0 lanes; the partner lane 32 apart holds channel
+    // 8 * CHUNKS + 4 there, which is zero, so the pair sum is the row sum.
+    constexpr int c0 = 8 * CHUNKS - 32 * (MBLK - 1);
+    static_assert(c0 % 8 == 0, "ones column on a chunk boundary");
+    l_own = oacc[MBLK - 1][(c0 / 8) * 4];
+  }
+  const float l_tot = sum_with_partner32(l_own);
   const bool empty = PADDED && !(l_tot > 0.f);  // no valid key: O = 0, lse = -inf
   const float inv = empty ? 0.f : 1.0f / l_tot;
   if (row_ok) {
