@@ -184,16 +184,33 @@ class Step:
         self.attention()
 
 
-def time_gpu(step: Step, steps: int, warmup: int):
+def ramp_clocks(torch, run, min_s: float) -> int:
+    """Run `run()` in batches of ten until at least `min_s` seconds of wall
+    time have passed with the GPU busy, and return how many calls that took.
+    A few milliseconds of warm-up leave the shader clock below where it
+    settles: the first timed pass after ten headline steps came out about
+    2 % slower than the passes after it."""
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < min_s:
+        for _ in range(10):
+            run()
+        n += 10
+        torch.cuda.synchronize()
+    return n
+
+
+def time_gpu(step: Step, steps: int, warmup: int, ramp_s: float = 0.3):
     """The step time comes from `steps` back-to-back steps bracketed by one
     pair of HIP events on the launch stream (and the host wall clock), with a
     synchronisation on both sides; a second pass of `steps` steps with events
     between the kernels gives the per-kernel breakdown (those events are not
-    inside the step time)."""
+    inside the step time).  Before it: `warmup` steps, then whole steps until
+    `ramp_s` seconds have passed (the clock ramp)."""
     torch = step.torch
     for _ in range(warmup):
         step.run()
     step.meta.check()
+    ramp_steps = ramp_clocks(torch, step.run, ramp_s)
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -218,7 +235,7 @@ def time_gpu(step: Step, steps: int, warmup: int):
     meta_ms = float(np.mean([a.elapsed_time(b) for a, b, _, _ in ev]))
     norm_ms = float(np.mean([b.elapsed_time(c) for _, b, c, _ in ev]))
     attn_ms = [c.elapsed_time(d) for _, _, c, d in ev]
-    return {"wall_ms_per_step": 1e3 * wall / steps, "step_ms": step_ms,
+    return {"wall_ms_per_step": 1e3 * wall / steps, "step_ms": step_ms, "ramp_steps": ramp_steps,
             "step_ms_with_kernel_events": ev[0][0].elapsed_time(ev[-1][3]) / steps, "meta_ms": meta_ms,
             "norm_ms": norm_ms, "attn_ms_mean": float(np.mean(attn_ms)), "attn_ms_min": float(np.min(attn_ms)),
             "attn_ms_median": float(np.median(attn_ms))}
@@ -338,7 +355,8 @@ def cpu_baseline(w: wl.Workload, drawn: wl.Drawn, budget_s: float = 12.0, text_v
             "seconds": elapsed}
 
 
-def bench_cfg(name: str, steps: int, warmup: int, cpu_budget: float, no_cpu: bool) -> dict:
+def bench_cfg(name: str, steps: int, warmup: int, cpu_budget: float, no_cpu: bool,
+              ramp_s: float = 0.3) -> dict:
     """The norm-rescaled guidance step on its own: `steps` back-to-back
     launches rotating over enough (cond, uncond, out) copies that one launch's
     data were not touched by the launches just before it (more than the 256 MB
@@ -363,6 +381,8 @@ def bench_cfg(name: str, steps: int, warmup: int, cpu_budget: float, no_cpu: boo
     stream = torch.cuda.current_stream()
     for i in range(warmup):
         dit.cfg_norm_rescale(conds[i % copies], uncs[i % copies], w.guidance, out=outs[i % copies])
+    ramp_steps = ramp_clocks(torch, lambda: dit.cfg_norm_rescale(conds[0], uncs[0], w.guidance, out=outs[0]),
+                             ramp_s)
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record(stream)
@@ -387,6 +407,7 @@ def bench_cfg(name: str, steps: int, warmup: int, cpu_budget: float, no_cpu: boo
                    "step": "uncond + s (cond - uncond), rescaled per token to ||cond||"},
         "per_launch_events": {"ms_median": float(np.median(ms)), "ms_min": float(np.min(ms))},
         "rotated_copies": copies,
+        "clock_ramp": {"seconds": ramp_s, "launches": ramp_steps},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": gbs / PEAK_HBM_GBS, "traffic": measured_traffic(w, CFG_TRAFFIC_FILE, CFG_SOURCE),
                      "kernel": "cfg_norm_rescale_kernel",
@@ -492,6 +513,9 @@ def main(argv=None) -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--clock-ramp-s", type=float, default=0.3, metavar="S",
+                    help="after the warm-up steps, keep running untimed steps until S seconds have passed, so "
+                         "that the timed steps run at the settled clock")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=list(wl.WORKLOADS) + list(wl.VARIANTS))
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the host oracle timing")
     ap.add_argument("--multistep", type=int, default=0, metavar="N",
@@ -529,7 +553,8 @@ def main(argv=None) -> int:
         return 2
 
     if args.cfg:
-        print(json.dumps(bench_cfg(args.cfg, args.steps, args.warmup, args.cpu_budget, args.no_cpu_baseline)),
+        print(json.dumps(bench_cfg(args.cfg, args.steps, args.warmup, args.cpu_budget, args.no_cpu_baseline,
+                                   args.clock_ramp_s)),
               flush=True)
         return 0
 
@@ -572,7 +597,7 @@ def main(argv=None) -> int:
     flops = 4.0 * w.head_dim * pairs * w.heads
     log("useful pairs per head (batch summed) %d  useful FLOPs/step %.4e" % (pairs, flops))
 
-    t = time_gpu(step, args.steps, args.warmup)
+    t = time_gpu(step, args.steps, args.warmup, args.clock_ramp_s)
     log("timing: %s" % json.dumps(t))
     cold = time_norm_cold(step)
     log("norm/rope with rotated inputs: %s" % json.dumps(cold))
@@ -616,6 +641,7 @@ def main(argv=None) -> int:
                    "compute_units": props.multi_processor_count},
         "token_metadata_ms": t["meta_ms"],
         "step_timing": {"host_wall_ms_per_step": t["wall_ms_per_step"],
+                        "clock_ramp": {"seconds": args.clock_ramp_s, "steps": t["ramp_steps"]},
                         "ms_per_step_with_kernel_events": t["step_ms_with_kernel_events"]},
         "roofline": roofline,
         "cpu_baseline": None,
