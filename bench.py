@@ -187,9 +187,10 @@ class Step:
 def ramp_clocks(torch, run, min_s: float) -> int:
     """Run `run()` in batches of ten until at least `min_s` seconds of wall
     time have passed with the GPU busy, and return how many calls that took.
-    A few milliseconds of warm-up leave the shader clock below where it
-    settles: the first timed pass after ten headline steps came out about
-    2 % slower than the passes after it."""
+    A few milliseconds of work after start-up, or after the GPU has idled
+    while the host did other work, leave the shader clock below where it
+    settles: a timed pass right after ten headline steps came out 2-7 %
+    slower than the passes after it."""
     n, t0 = 0, time.perf_counter()
     while time.perf_counter() - t0 < min_s:
         for _ in range(10):
@@ -241,7 +242,7 @@ def time_gpu(step: Step, steps: int, warmup: int, ramp_s: float = 0.3):
             "attn_ms_median": float(np.median(attn_ms))}
 
 
-def time_norm_cold(step: Step, reps: int = 30, copies: int = 3):
+def time_norm_cold(step: Step, reps: int = 30, copies: int = 3, ramp_s: float = 0.3):
     """K2 alone, rotating `copies` separate input copies so that the Q/K read
     by one launch were not touched by the launches just before it (config
     3's Q+K, 168 MB, would otherwise partly stay in the 256 MB Infinity
@@ -255,6 +256,7 @@ def time_norm_cold(step: Step, reps: int = 30, copies: int = 3):
         step.norm_launch(qs[i % copies], ks[i % copies], step.meta.pos_ids[P:], step.qp, step.kp)
     for i in range(copies):
         launch(i)
+    ramp_clocks(torch, lambda: launch(0), ramp_s)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     torch.cuda.synchronize()
     for i, (a, b) in enumerate(ev):
@@ -267,7 +269,7 @@ def time_norm_cold(step: Step, reps: int = 30, copies: int = 3):
     return {"ms_mean": float(np.mean(ms)), "ms_median": float(np.median(ms)), "ms_min": float(np.min(ms))}
 
 
-def multistep(step: Step, n_steps: int, reps: int, warmup: int, full_ms: float):
+def multistep(step: Step, n_steps: int, reps: int, warmup: int, full_ms: float, ramp_s: float = 0.3):
     """Step 1 runs the whole joint sequence; its norm kernel writes K' of every
     token, so rows [0, P) of that buffer are the cache (P = every token before
     the target block: text and condition images, which do not change with the
@@ -295,16 +297,27 @@ def multistep(step: Step, n_steps: int, reps: int, warmup: int, full_ms: float):
         cached()
     torch.cuda.synchronize()
     same = bool(torch.equal(o_new, step.o[:, P:]))
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for a, b in ev:
-        a.record(step.stream)
+    ramp_clocks(torch, cached, ramp_s)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(step.stream)
+    for _ in range(reps):
         cached()
-        b.record(step.stream)
+    t1.record(step.stream)
     torch.cuda.synchronize()
-    cached_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    cached_ms = t0.elapsed_time(t1) / reps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+    for e in ev:
+        e[0].record(step.stream)
+        step.norm_launch(q_new, k_new, step.meta.pos_ids[P:], qp_new, kp_new)
+        e[1].record(step.stream)
+        step.attention_launch(q_new, qp_new, k_cache, v_cache, kp_new, v_new, o_new, step.meta.pos_ids[P:])
+        e[2].record(step.stream)
+    torch.cuda.synchronize()
     amort = (full_ms + (n_steps - 1) * cached_ms) / n_steps
     return {"steps": n_steps, "prefix_tokens": P, "target_tokens": w.seq_len - P, "full_step_ms": full_ms,
             "cached_step_ms": cached_ms, "amortised_ms_per_step": amort, "speedup_vs_full_steps": full_ms / amort,
+            "cached_norm_ms": float(np.mean([a.elapsed_time(b) for a, b, _ in ev])),
+            "cached_attention_ms": float(np.mean([b.elapsed_time(c) for _, b, c in ev])),
             "cached_rows_equal_full_rows": same}
 
 
@@ -599,7 +612,7 @@ def main(argv=None) -> int:
 
     t = time_gpu(step, args.steps, args.warmup, args.clock_ramp_s)
     log("timing: %s" % json.dumps(t))
-    cold = time_norm_cold(step)
+    cold = time_norm_cold(step, ramp_s=args.clock_ramp_s)
     log("norm/rope with rotated inputs: %s" % json.dumps(cold))
     props = torch.cuda.get_device_properties(0)
     value = flops / (t["step_ms"] * 1e-3) / 1e12
@@ -651,7 +664,7 @@ def main(argv=None) -> int:
                                           "valid_per_sample": step.tv.sum(axis=1).tolist()}
         line["config"]["step"] = "token metadata + key validity + qk-rmsnorm/rope + padded attention"
     if args.multistep:
-        ms = multistep(step, args.multistep, args.steps, args.warmup, t["step_ms"])
+        ms = multistep(step, args.multistep, args.steps, args.warmup, t["step_ms"], args.clock_ramp_s)
         log("multistep: %s" % json.dumps(ms))
         line["multistep"] = ms
     if not args.no_cpu_baseline:
