@@ -177,7 +177,7 @@ __global__ __launch_bounds__(kThreads) void qknorm_rope_kernel(QkNormRopeArgs a)
 // through LDS: each item stores its partial, and after a barrier each item
 // adds the CPH partials of its head.
 constexpr int kFlatItems = 4;  // items per thread kept in flight
-constexpr int kFlatTokens = 4; // most tokens per work-group
+constexpr int kFlatTokens = 16; // most tokens per work-group
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void qknorm_rope_flat_kernel(QkNormRopeArgs a, int tpw) {
@@ -434,19 +434,20 @@ hipError_t launch_typed(const QkNormRopeArgs& a, hipStream_t stream) {
   constexpr int EPC = Elem<T>::kPerChunk;
   const int chunks = a.D / EPC;
   const int per_tok = (a.H + a.Hk) * chunks;
-  // Tokens per work-group: the count (1, 2 or 4) that leaves the fewest idle
-  // item slots, within the items a work-group keeps in flight.
+  // Tokens per work-group: the count (1..16) that leaves the fewest idle item
+  // slots per token, within the items a work-group keeps in flight.  A small
+  // token (8 KV heads x 9 chunks) thus shares its work-group with 13 others
+  // instead of leaving most of the slots idle.
   // A power-of-two chunk count fills whole lane groups: one head per group
   // with a butterfly sum is faster there.
   int tpw = 0;
-  long best = -1;
+  long best_idle = 0;
   const bool pow2 = (chunks & (chunks - 1)) == 0;
-  for (int t = 1; !pow2 && t <= kFlatTokens; t *= 2) {
+  for (int t = 1; !pow2 && t <= kFlatTokens; ++t) {
     const long items = (long)t * per_tok;
     if (items > (long)kThreads * kFlatItems) break;
-    const long slots = (items + kThreads - 1) / kThreads * kThreads;
-    const long waste = (slots - items) * 4 / t;  // idle slots per token
-    if (best < 0 || waste < best) { best = waste; tpw = t; }
+    const long idle = (items + kThreads - 1) / kThreads * kThreads - items;
+    if (tpw == 0 || idle * tpw < best_idle * t) { best_idle = idle; tpw = t; }  // idle / t < best_idle / tpw
   }
   if (tpw > 0) {
     dim3 grid((a.S + tpw - 1) / tpw, a.B);

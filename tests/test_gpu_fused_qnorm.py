@@ -171,6 +171,8 @@ def test_k_only_norm_every_kernel(dit):
     cases = [
         (2, 32, 8, 128, (16, 56, 56), "rms_per_head", 1.0, 1.0),      # per-head kernel
         (3, 2, 1, 48, (16, 16, 16), "rms_per_head", 1.0, 1.0),        # flat kernel (6 chunks per head)
+        (2, 32, 8, 72, (24, 24, 24), "rms_per_head", 1.0, 2.0),       # flat, 7 tokens per work-group
+        (1, 6, 3, 72, (24, 24, 24), "rms_per_head", 1.0, 1.0),        # flat, 3 tokens per work-group
         (2, 4, 2, 72, (24, 24, 24), "layer_across_heads", 2.0, 1.0),
         (1, 4, 4, 64, (16, 24, 24), "rms_per_head", 1.0, 3.0),
     ]
