@@ -244,9 +244,9 @@ def time_gpu(step: Step, steps: int, warmup: int, ramp_s: float = 0.3):
 
 def time_norm_cold(step: Step, reps: int = 30, copies: int = 3, ramp_s: float = 0.3):
     """K2 alone, rotating `copies` separate input copies so that the Q/K read
-    by one launch were not touched by the launches just before it (config
-    3's Q+K, 168 MB, would otherwise partly stay in the 256 MB Infinity
-    Cache)."""
+    by one launch were not touched by the launches just before it (the
+    headline workload's Q+K, 168 MB, or its K alone with K', would
+    otherwise partly stay in the 256 MB Infinity Cache)."""
     torch, w = step.torch, step.w
     P = w.prefix_len
     qs = [step.q] + [step.q.clone() for _ in range(copies - 1)]
