@@ -126,3 +126,24 @@ def test_counter_summary_scales_by_the_copy_calibration(tmp_path, monkeypatch):
     assert att["write_bytes"] == pytest.approx(32.0 * 1024 * ws)
     assert rec["hbm_bytes_per_launch"] == pytest.approx(att["fetch_bytes"] + att["write_bytes"])
     assert rec["kernels"]["qknorm_rope"]["hbm_bytes"] == pytest.approx(40.0 * 1024 * (fs + ws))
+
+
+def test_clock_ramp_runs_whole_batches_until_the_time_is_up():
+    """The clock ramp runs untimed calls in batches of ten, synchronising after
+    each batch, until its wall-clock floor has passed; it reports the calls."""
+    class _Cuda:
+        syncs = 0
+
+        @classmethod
+        def synchronize(cls):
+            cls.syncs += 1
+
+    class _Torch:
+        cuda = _Cuda
+
+    calls = []
+    n = bench.ramp_clocks(_Torch, lambda: calls.append(1), 0.02)
+    assert n == len(calls) and n >= 10 and n % 10 == 0
+    assert _Cuda.syncs == n // 10
+    _Cuda.syncs = 0
+    assert bench.ramp_clocks(_Torch, lambda: None, 0.0) == 0 and _Cuda.syncs == 0
