@@ -54,7 +54,10 @@ constexpr int kRowBytes = 256;    // LDS bytes per key row (16 chunks of 16 B)
 constexpr int kTileBytes = kTileN * kRowBytes;
 constexpr float kLazyRescale = 8.0f;  // log2 units
 constexpr int PF_K = 3;  // K operands read this many MFMAs ahead
-constexpr int PF_V = 2;  // V^T operands read this many MFMAs ahead
+// V^T operands read this many MFMAs ahead: 2, or 3 in the 80-channel variant
+// (12 PV MFMAs per tile; one more read in flight measured 0.6 % faster there,
+// while at 128 channels 3 is no better and the cached-prefix workload slows).
+constexpr int pf_v(int dp) { return dp == 80 ? 3 : 2; }
 
 __device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 
@@ -134,6 +137,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   // contraction steps, not six); O^T runs in 32-channel blocks, so its last
   // block may reach past DP, where the tiles hold zeros.
   static_assert(DP % 16 == 0 && DP >= 32 && DP <= 128, "padded head dim");
+  constexpr int PF_V = pf_v(DP);
   constexpr int KSTEPS = DP / 16;         // QK^T contraction steps
   constexpr int MBLK = (DP + 31) / 32;    // 32-channel blocks of O^T
   constexpr int CHUNKS = DP / 8;          // 16-byte chunks per key row actually used
