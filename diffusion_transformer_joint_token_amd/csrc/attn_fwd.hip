@@ -71,27 +71,35 @@ __device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >>
 // the same way, so light tiles fill the tail instead of delaying heavy ones
 // and each unit's keys are re-read at most once.  Under the full mask every
 // tile does the same work and the order is unit by unit.
-__device__ __forceinline__ void map_block(int id, int nblocks, int n_qtiles, bool causal, int& bh, int& qtile) {
+// Units are dealt head-major, (head, sample), so each XCD holds the same
+// heads of every sample: samples whose padded text leaves them fewer keys
+// then do not all land on the same XCDs, which would finish early while the
+// others set the launch time.  Query heads that share a KV head stay on one
+// XCD.
+__device__ __forceinline__ void map_block(int id, int nblocks, int n_qtiles, bool causal, int B, int H, int& bh,
+                                          int& qtile) {
   const int per = nblocks >> 3;
+  int unit;
   if (id < per * 8 && per % n_qtiles == 0) {
     const int x = id & 7, j = id >> 3;  // XCD, position in its queue
     const int units = per / n_qtiles;
     const int low = causal ? n_qtiles / 5 : 0;
     const int hi = n_qtiles - low;
     if (j < units * hi) {
-      bh = x * units + j / hi;
+      unit = x * units + j / hi;
       qtile = n_qtiles - 1 - j % hi;
     } else {
       const int k = j - units * hi;
-      bh = x * units + k / low;
+      unit = x * units + k / low;
       qtile = low - 1 - k % low;
     }
-    return;
+  } else {
+    int logical = id;
+    if (id < per * 8) logical = (id & 7) * per + (id >> 3);
+    unit = logical / n_qtiles;
+    qtile = n_qtiles - 1 - (logical - unit * n_qtiles);
   }
-  int logical = id;
-  if (id < per * 8) logical = (id & 7) * per + (id >> 3);
-  bh = logical / n_qtiles;
-  qtile = n_qtiles - 1 - (logical - bh * n_qtiles);
+  bh = (unit % B) * H + unit / B;  // unit = head * B + sample
 }
 
 // Buffer resource word 3 for untyped 32-bit accesses on gfx9-class parts.
@@ -163,7 +171,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   const int g = lane >> 5;  // k-group of the MFMA operands
   const int n_qtiles = (a.Snew + 32 * NW - 1) / (32 * NW);
   int bh, qtile;
-  map_block(blockIdx.x, gridDim.x, n_qtiles, a.kv_limit != nullptr, bh, qtile);
+  map_block(blockIdx.x, gridDim.x, n_qtiles, a.kv_limit != nullptr, a.B, a.H, bh, qtile);
   const int h = bh % a.H;
   const int b = bh / a.H;
   const int kvh = h / (a.H / a.Hk);
