@@ -275,96 +275,130 @@ __global__ __launch_bounds__(kThreads) void qknorm_rope_flat_kernel(QkNormRopeAr
   }
 }
 
-// LayerNorm across heads: one token per work-group; item k of thread t is
-// (head, chunk) number t + 256 k, Q heads first.
+// LayerNorm across heads: TOK tokens per work-group; item k of thread t is
+// (head, chunk) number t + 256 k of each token, Q heads first, so a thread
+// loads each channel's weight and bias once for all its tokens.
 constexpr int kLnMaxItems = 8;
 
-// Sum of a Q partial and a K partial over the work-group, in a fixed order.
-__device__ __forceinline__ float2 block_sum2(float vq, float vk, float2 (*red)[kThreads / 64]) {
+// Per token, the sum of a Q partial and of a K partial over the work-group,
+// in a fixed order (the same tree for any TOK).
+template <int TOK>
+__device__ __forceinline__ void block_sums(float (&vq)[TOK], float (&vk)[TOK], float2 (*red)[TOK][kThreads / 64]) {
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    vq += __shfl_xor(vq, m, 64);
-    vk += __shfl_xor(vk, m, 64);
-  }
+  for (int t = 0; t < TOK; ++t)
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      vq[t] += __shfl_xor(vq[t], m, 64);
+      vk[t] += __shfl_xor(vk[t], m, 64);
+    }
   const int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) (*red)[wave] = make_float2(vq, vk);
-  __syncthreads();
-  float2 t = (*red)[0];
+  if ((threadIdx.x & 63) == 0)
 #pragma unroll
-  for (int w = 1; w < kThreads / 64; ++w) {
-    t.x += (*red)[w].x;
-    t.y += (*red)[w].y;
+    for (int t = 0; t < TOK; ++t) (*red)[t][wave] = make_float2(vq[t], vk[t]);
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < TOK; ++t) {
+    float2 u = (*red)[t][0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) {
+      u.x += (*red)[t][w].x;
+      u.y += (*red)[t][w].y;
+    }
+    vq[t] = u.x;
+    vk[t] = u.y;
   }
-  return t;
 }
 
-template <typename T, int ITEMS>
+template <typename T, int ITEMS, int TOK>
 __global__ __launch_bounds__(kThreads) void qk_layernorm_rope_kernel(QkNormRopeArgs a) {
   constexpr int EPC = Elem<T>::kPerChunk;
-  __shared__ float2 s_cs[kMaxPairs];
-  __shared__ float2 s_red[2][kThreads / 64];
+  __shared__ float2 s_cs[TOK][kMaxPairs];
+  __shared__ float2 s_red[2][TOK][kThreads / 64];
 
   const int tid = threadIdx.x;
-  const int s = blockIdx.x;
+  const int s0 = blockIdx.x * TOK;
   const int b = blockIdx.y;
   const int D = a.D;
   const int cph = D / EPC;
   const int nq = a.H * cph;
   const int n = (a.H + a.Hk) * cph;
 
-  u32x4 raw[ITEMS];
+  u32x4 raw[TOK][ITEMS];
 #pragma unroll
-  for (int k = 0; k < ITEMS; ++k) {
-    const int item = tid + k * kThreads;
-    raw[k] = u32x4{0, 0, 0, 0};
-    if (item < n) {
-      const int vh = item / cph, c = item - vh * cph;
-      const T* src;
-      if (vh < a.H)
-        src = reinterpret_cast<const T*>(a.q) + b * a.qs[0] + (int64_t)s * a.qs[1] + vh * a.qs[2];
-      else
-        src = reinterpret_cast<const T*>(a.k) + b * a.ks[0] + (int64_t)s * a.ks[1] + (vh - a.H) * a.ks[2];
-      raw[k] = *reinterpret_cast<const u32x4*>(src + c * EPC);
+  for (int t = 0; t < TOK; ++t)
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k) {
+      const int item = tid + k * kThreads;
+      const int s = s0 + t;
+      raw[t][k] = u32x4{0, 0, 0, 0};
+      if (item < n && s < a.S) {
+        const int vh = item / cph, c = item - vh * cph;
+        const T* src;
+        if (vh < a.H)
+          src = reinterpret_cast<const T*>(a.q) + b * a.qs[0] + (int64_t)s * a.qs[1] + vh * a.qs[2];
+        else
+          src = reinterpret_cast<const T*>(a.k) + b * a.ks[0] + (int64_t)s * a.ks[1] + (vh - a.H) * a.ks[2];
+        raw[t][k] = *reinterpret_cast<const u32x4*>(src + c * EPC);
+      }
     }
-  }
-  if (tid < D / 2) {  // rotary phases of this token, as in the per-head kernel
-    const int ax = a.pair_axis[tid];
+  if (tid < TOK * (D / 2)) {  // rotary phases of these tokens, as in the per-head kernel
+    const int t = tid / (D / 2), j = tid - t * (D / 2);
+    const int s = min(s0 + t, a.S - 1);
     float sn, cs;
-    sincos_turns((double)a.pos[3 * s + ax] * a.omega[tid], sn, cs);
-    s_cs[tid] = make_float2(cs, sn);
+    sincos_turns((double)a.pos[3 * s + a.pair_axis[j]] * a.omega[j], sn, cs);
+    s_cs[t][j] = make_float2(cs, sn);
   }
 
-  // Mean of the token's Q channels and of its K channels.
-  float x[ITEMS][EPC];
-  float sq = 0.f, sk = 0.f;
+  // Mean of each token's Q channels and of its K channels.
+  float x[TOK][ITEMS][EPC];
+  float sq[TOK], sk[TOK];
 #pragma unroll
-  for (int k = 0; k < ITEMS; ++k) {
-    Elem<T>::unpack(raw[k], x[k]);
-    float t = 0.f;
+  for (int t = 0; t < TOK; ++t) {
+    sq[t] = 0.f;
+    sk[t] = 0.f;
 #pragma unroll
-    for (int i = 0; i < EPC; ++i) t += x[k][i];
-    if (tid + k * kThreads < nq) sq += t; else sk += t;  // items past n hold zeros
-  }
-  const float2 tot = block_sum2(sq, sk, &s_red[0]);
-  const float mq = tot.x / (float)(a.H * D), mk = tot.y / (float)(a.Hk * D);
-  // Centred variance.
-  float vq = 0.f, vk = 0.f;
+    for (int k = 0; k < ITEMS; ++k) {
+      Elem<T>::unpack(raw[t][k], x[t][k]);
+      float u = 0.f;
 #pragma unroll
-  for (int k = 0; k < ITEMS; ++k) {
-    const int item = tid + k * kThreads;
-    if (item >= n) continue;
-    const float m = item < nq ? mq : mk;
-    float t = 0.f;
-#pragma unroll
-    for (int i = 0; i < EPC; ++i) {
-      const float d = x[k][i] - m;
-      t = fmaf(d, d, t);
+      for (int i = 0; i < EPC; ++i) u += x[t][k][i];
+      if (tid + k * kThreads < nq) sq[t] += u; else sk[t] += u;  // items past n hold zeros
     }
-    if (item < nq) vq += t; else vk += t;
   }
-  const float2 var = block_sum2(vq, vk, &s_red[1]);
-  const float rq = 1.0f / sqrtf(var.x / (float)(a.H * D) + a.eps);
-  const float rk = 1.0f / sqrtf(var.y / (float)(a.Hk * D) + a.eps);
+  block_sums<TOK>(sq, sk, &s_red[0]);
+  float mq[TOK], mk[TOK];
+#pragma unroll
+  for (int t = 0; t < TOK; ++t) {
+    mq[t] = sq[t] / (float)(a.H * D);
+    mk[t] = sk[t] / (float)(a.Hk * D);
+  }
+  // Centred variance.
+  float vq[TOK], vk[TOK];
+#pragma unroll
+  for (int t = 0; t < TOK; ++t) {
+    vq[t] = 0.f;
+    vk[t] = 0.f;
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k) {
+      const int item = tid + k * kThreads;
+      if (item >= n) continue;
+      const float m = item < nq ? mq[t] : mk[t];
+      float u = 0.f;
+#pragma unroll
+      for (int i = 0; i < EPC; ++i) {
+        const float d = x[t][k][i] - m;
+        u = fmaf(d, d, u);
+      }
+      if (item < nq) vq[t] += u; else vk[t] += u;
+    }
+  }
+  block_sums<TOK>(vq, vk, &s_red[1]);
+  float rq[TOK], rk[TOK];
+#pragma unroll
+  for (int t = 0; t < TOK; ++t) {
+    rq[t] = 1.0f / sqrtf(vq[t] / (float)(a.H * D) + a.eps);
+    rk[t] = 1.0f / sqrtf(vk[t] / (float)(a.Hk * D) + a.eps);
+  }
 
 #pragma unroll
   for (int k = 0; k < ITEMS; ++k) {
@@ -390,23 +424,29 @@ __global__ __launch_bounds__(kThreads) void qk_layernorm_rope_kernel(QkNormRopeA
         for (int i = 0; i < EPC; ++i) bv[i] = 0.0f;
       }
     }
-    const float m = is_q ? mq : mk, r = is_q ? rq : rk, sc = is_q ? a.q_scale : 1.0f;
-    float y[EPC];
+    const float sc = is_q ? a.q_scale : 1.0f;
 #pragma unroll
-    for (int i = 0; i < EPC; ++i) y[i] = fmaf((x[k][i] - m) * r, wv[i], bv[i]) * sc;
+    for (int t = 0; t < TOK; ++t) {
+      const int s = s0 + t;
+      if (s >= a.S) continue;
+      const float m = is_q ? mq[t] : mk[t], r = is_q ? rq[t] : rk[t];
+      float y[EPC];
 #pragma unroll
-    for (int i = 0; i < EPC / 2; ++i) {
-      const float2 cs = s_cs[(c * EPC) / 2 + i];
-      const float y0 = y[2 * i], y1 = y[2 * i + 1];
-      y[2 * i] = y0 * cs.x - y1 * cs.y;
-      y[2 * i + 1] = y0 * cs.y + y1 * cs.x;
+      for (int i = 0; i < EPC; ++i) y[i] = fmaf((x[t][k][i] - m) * r, wv[i], bv[i]) * sc;
+#pragma unroll
+      for (int i = 0; i < EPC / 2; ++i) {
+        const float2 cs = s_cs[t][(c * EPC) / 2 + i];
+        const float y0 = y[2 * i], y1 = y[2 * i + 1];
+        y[2 * i] = y0 * cs.x - y1 * cs.y;
+        y[2 * i + 1] = y0 * cs.y + y1 * cs.x;
+      }
+      T* dst;
+      if (is_q)
+        dst = reinterpret_cast<T*>(a.qo) + b * a.qos[0] + (int64_t)s * a.qos[1] + vh * a.qos[2];
+      else
+        dst = reinterpret_cast<T*>(a.ko) + b * a.kos[0] + (int64_t)s * a.kos[1] + (vh - a.H) * a.kos[2];
+      *reinterpret_cast<u32x4*>(dst + c * EPC) = Elem<T>::pack(y);
     }
-    T* dst;
-    if (is_q)
-      dst = reinterpret_cast<T*>(a.qo) + b * a.qos[0] + (int64_t)s * a.qos[1] + vh * a.qos[2];
-    else
-      dst = reinterpret_cast<T*>(a.ko) + b * a.kos[0] + (int64_t)s * a.kos[1] + (vh - a.H) * a.kos[2];
-    *reinterpret_cast<u32x4*>(dst + c * EPC) = Elem<T>::pack(y);
   }
 }
 
@@ -414,15 +454,17 @@ template <typename T>
 hipError_t launch_layernorm(const QkNormRopeArgs& a, hipStream_t stream) {
   constexpr int EPC = Elem<T>::kPerChunk;
   const int n = (a.H + a.Hk) * (a.D / EPC);
-  const dim3 grid(a.S, a.B);
+  // Two tokens per work-group while a thread holds at most two items of each,
+  // so each thread keeps up to four loads in flight.
+  const dim3 grid1(a.S, a.B), grid2((a.S + 1) / 2, a.B);
   if (n <= kThreads)
-    hipLaunchKernelGGL((qk_layernorm_rope_kernel<T, 1>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((qk_layernorm_rope_kernel<T, 1, 2>), grid2, dim3(kThreads), 0, stream, a);
   else if (n <= 2 * kThreads)
-    hipLaunchKernelGGL((qk_layernorm_rope_kernel<T, 2>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((qk_layernorm_rope_kernel<T, 2, 2>), grid2, dim3(kThreads), 0, stream, a);
   else if (n <= 4 * kThreads)
-    hipLaunchKernelGGL((qk_layernorm_rope_kernel<T, 4>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((qk_layernorm_rope_kernel<T, 4, 1>), grid1, dim3(kThreads), 0, stream, a);
   else if (n <= kLnMaxItems * kThreads)
-    hipLaunchKernelGGL((qk_layernorm_rope_kernel<T, kLnMaxItems>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((qk_layernorm_rope_kernel<T, kLnMaxItems, 1>), grid1, dim3(kThreads), 0, stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
