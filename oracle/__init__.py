@@ -37,6 +37,11 @@ float64 NumPy, slow and plain:
   validity, which ``attention`` and ``attention_bruteforce`` take as
   ``key_valid`` (QwenImage21Transformer2DModel API page, ``forward``).
 
+* ``pipeline.step`` / ``pipeline.extract_cache`` -- the composed step
+  (norm and rotation of the query tokens at their logical positions, then the
+  masked attention) in the full and the cached form, and the "extract" mode's
+  cache (QwenImage21Transformer2DModel API page, forward's kv_cache modes).
+
 * ``cfg.norm_rescaled_cfg`` -- classifier-free guidance whose mixed
   prediction is rescaled, token by token, to the norm of the conditional one
   (NucleusMoE-Image pipeline article, section 4.3).

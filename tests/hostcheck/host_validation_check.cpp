@@ -1,0 +1,466 @@
+// Host-side argument validation of the C ABI, built for the CPU alone with
+// AddressSanitizer and UndefinedBehaviorSanitizer (g++), linked against
+// stand-in launchers that record what would have been launched instead of
+// touching a GPU.  The cases mirror tests/test_abi.py (every argument error is
+// returned before anything is enqueued) and add the accepted calls, whose
+// launch arguments are checked: buffer pointers, strides, the folded softmax
+// scale, the rotary frequencies.
+//
+// Build and run (tests/test_hostcheck.py does this):
+//   g++ -std=c++17 -O1 -g -fsanitize=address,undefined -fno-sanitize-recover=all
+//       -D__HIP_PLATFORM_AMD__ -I/opt/rocm/include -I include
+//       diffusion_transformer_joint_token_amd/csrc/api.cpp
+//       tests/hostcheck/host_validation_check.cpp -o <tmp>/hostcheck
+// Exit status 0 and "hostcheck: N cases passed" on success.
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <limits>
+#include <vector>
+
+#include "../../diffusion_transformer_joint_token_amd/csrc/kernels.h"
+#include "dit_attn.h"
+
+// ---------------------------------------------------------------- stand-in launchers
+namespace {
+int g_launches = 0;
+dit::AttnArgs g_attn{};
+int g_attn_dtype = -1;
+dit::QkNormRopeArgs g_norm{};
+dit::TokenMetaArgs g_meta{};
+dit::KeyValidArgs g_kv{};
+dit::CfgArgs g_cfg{};
+}  // namespace
+
+namespace dit {
+hipError_t launch_token_meta(const uint8_t*, const TokenMetaArgs& a, int32_t*, uint8_t*, int32_t*, int32_t*,
+                             int32_t*, hipStream_t) {
+  ++g_launches;
+  g_meta = a;
+  return hipSuccess;
+}
+hipError_t launch_key_valid(const KeyValidArgs& a, hipStream_t) {
+  ++g_launches;
+  g_kv = a;
+  return hipSuccess;
+}
+hipError_t launch_qknorm_rope(const QkNormRopeArgs& a, int, hipStream_t) {
+  ++g_launches;
+  g_norm = a;
+  return hipSuccess;
+}
+hipError_t launch_attention(const AttnArgs& a, int dtype, hipStream_t) {
+  ++g_launches;
+  g_attn = a;
+  g_attn_dtype = dtype;
+  return hipSuccess;
+}
+hipError_t launch_cfg_norm_rescale(const CfgArgs& a, int, hipStream_t) {
+  ++g_launches;
+  g_cfg = a;
+  return hipSuccess;
+}
+}  // namespace dit
+
+// ---------------------------------------------------------------- checking
+namespace {
+int g_cases = 0, g_failed = 0;
+
+// An argument error: the expected status and nothing launched.
+void expect_error(const char* what, int got, int want) {
+  ++g_cases;
+  if (got != want) {
+    ++g_failed;
+    std::printf("FAIL %s: status %d, expected %d\n", what, got, want);
+  }
+}
+
+void expect(const char* what, bool ok) {
+  ++g_cases;
+  if (!ok) {
+    ++g_failed;
+    std::printf("FAIL %s\n", what);
+  }
+}
+
+// Argument-error checks: the call must return `want` and launch nothing.
+#define ERR(call, want)                                   \
+  do {                                                    \
+    const int before_ = g_launches;                       \
+    expect_error(#call, (call), (want));                  \
+    expect("no launch: " #call, g_launches == before_);   \
+  } while (0)
+
+// An accepted call: OK and exactly one launch (or none, for empty work).
+#define OK_LAUNCHES(call, n)                                       \
+  do {                                                             \
+    const int before_ = g_launches;                                \
+    expect_error(#call, (call), DIT_ATTN_OK);                      \
+    expect("launch count: " #call, g_launches == before_ + (n));  \
+  } while (0)
+
+// Distinct, 16-byte aligned, never dereferenced addresses (the launchers are
+// stand-ins, so no buffer is read).
+char* const FAKE = reinterpret_cast<char*>(0x100000);
+char* const FAKE2 = reinterpret_cast<char*>(0x200000);
+char* const FAKE3 = reinterpret_cast<char*>(0x300000);
+
+dit_attn_token_meta meta_of(int32_t seq_len) {
+  dit_attn_token_meta m;
+  m.image_ids = reinterpret_cast<int32_t*>(FAKE3);
+  m.target_mask = reinterpret_cast<uint8_t*>(FAKE3 + 0x10000);
+  m.pos_ids = reinterpret_cast<int32_t*>(FAKE3 + 0x20000);
+  m.kv_limit = reinterpret_cast<int32_t*>(FAKE3 + 0x40000);
+  m.seq_len = seq_len;
+  return m;
+}
+
+dit_attn_norm_rope_params params(int norm = DIT_ATTN_NORM_RMS_PER_HEAD) {
+  dit_attn_norm_rope_params p{};
+  p.norm = norm;
+  p.eps = 1e-6f;
+  p.rope_theta = 1e4f;
+  p.rope_linear_factor = 1.f;
+  p.rope_ntk_factor = 1.f;
+  p.q_scale = 1.f;
+  return p;
+}
+
+const float kInf = std::numeric_limits<float>::infinity();
+const float kNaN = std::numeric_limits<float>::quiet_NaN();
+
+void metadata_cases() {
+  dit_attn_token_meta m = meta_of(16);
+  const int32_t shapes[3] = {1, 4, 4};
+  auto f = [&](const uint8_t* mask, int32_t S, const int32_t* sh, int32_t n, int32_t mode,
+               const dit_attn_token_meta* mp, int32_t* st) {
+    return dit_attn_build_token_metadata(mask, S, sh, n, mode, mp, st, nullptr);
+  };
+  const uint8_t* mk = reinterpret_cast<const uint8_t*>(FAKE);
+  int32_t* st = reinterpret_cast<int32_t*>(FAKE2);
+  ERR(f(nullptr, 16, shapes, 1, 0, &m, st), DIT_ATTN_ERR_NULL);
+  ERR(f(mk, 16, shapes, 1, 0, nullptr, st), DIT_ATTN_ERR_NULL);
+  ERR(f(mk, 16, shapes, 1, 0, &m, nullptr), DIT_ATTN_ERR_NULL);
+  ERR(f(mk, 16, nullptr, 1, 0, &m, st), DIT_ATTN_ERR_NULL);
+  ERR(f(mk, 17, shapes, 1, 0, &m, st), DIT_ATTN_ERR_SHAPE);        // seq_len differs from meta
+  ERR(f(mk, 16, shapes, 65, 0, &m, st), DIT_ATTN_ERR_SHAPE);       // too many images
+  ERR(f(mk, 16, shapes, -1, 0, &m, st), DIT_ATTN_ERR_SHAPE);
+  ERR(f(mk, 16, shapes, 1, 7, &m, st), DIT_ATTN_ERR_UNSUPPORTED);  // pos mode
+  const int32_t odd[3] = {1, 3, 4};
+  ERR(f(mk, 16, odd, 1, 0, &m, st), DIT_ATTN_ERR_SHAPE);           // odd H, centred
+  const int32_t frames[3] = {2, 2, 2};
+  ERR(f(mk, 16, frames, 1, 1, &m, st), DIT_ATTN_ERR_SHAPE);        // 2 frames on the 2D grid
+  const int32_t big[6] = {1, 4, 4, 1, 2, 2};
+  ERR(f(mk, 16, big, 2, 0, &m, st), DIT_ATTN_ERR_SHAPE);           // 20 image tokens > 16
+  const int32_t zero[3] = {1, 0, 4};
+  ERR(f(mk, 16, zero, 1, 0, &m, st), DIT_ATTN_ERR_SHAPE);
+  const int32_t huge[3] = {1, 1 << 20, 1 << 20};                   // product overflows 32 bits
+  ERR(f(mk, 16, huge, 1, 0, &m, st), DIT_ATTN_ERR_SHAPE);
+  // Accepted: text 10 + a (2, 2, 4) block + text 6 = 32 tokens; the host
+  // folds the shapes into cumulative counts, frame offsets and max_vid.
+  dit_attn_token_meta m32 = meta_of(32);
+  const int32_t two[6] = {1, 2, 4, 1, 2, 2};
+  OK_LAUNCHES(f(mk, 32, two, 2, 0, &m32, st), 1);
+  expect("meta cum", g_meta.cum[0] == 0 && g_meta.cum[1] == 8 && g_meta.cum[2] == 12);
+  expect("meta frame offsets", g_meta.frame_off[0] == 0 && g_meta.frame_off[1] == 1);
+  // largest coordinate: frame 1, h/w up to 4/2 - 1 = 1 -> max_vid_index 2
+  expect("meta max_vid", g_meta.max_vid == 2);
+  OK_LAUNCHES(f(mk, 32, nullptr, 0, 0, &m32, st), 1);  // text only
+  expect("meta text only", g_meta.max_vid == 0 && g_meta.n_img == 0);
+}
+
+void key_valid_cases() {
+  const uint8_t* mk = reinterpret_cast<const uint8_t*>(FAKE);
+  const uint8_t* tv = reinterpret_cast<const uint8_t*>(FAKE3);
+  uint64_t* bits = reinterpret_cast<uint64_t*>(FAKE2);
+  int32_t* st = reinterpret_cast<int32_t*>(FAKE3 + 0x8000);
+  auto f = [&](const uint8_t* m, int32_t S, const uint8_t* t, int32_t B, int32_t n, int64_t ts, uint64_t* b,
+               int64_t w, int32_t* s) { return dit_attn_build_key_valid(m, S, t, B, n, ts, b, w, s, nullptr); };
+  ERR(f(nullptr, 5120, tv, 2, 1024, 1024, bits, 80, st), DIT_ATTN_ERR_NULL);
+  ERR(f(mk, 5120, nullptr, 2, 1024, 1024, bits, 80, st), DIT_ATTN_ERR_NULL);
+  ERR(f(mk, 5120, tv, 2, 1024, 1024, nullptr, 80, st), DIT_ATTN_ERR_NULL);
+  ERR(f(mk, 5120, tv, 2, 1024, 1024, bits, 80, nullptr), DIT_ATTN_ERR_NULL);
+  ERR(f(mk, 5120, tv, 2, 5121, 5121, bits, 80, st), DIT_ATTN_ERR_SHAPE);  // more text than tokens
+  ERR(f(mk, 5120, tv, 2, 1024, 1000, bits, 80, st), DIT_ATTN_ERR_SHAPE);  // rows overlap
+  ERR(f(mk, 5120, tv, 2, 1024, 1024, bits, 79, st), DIT_ATTN_ERR_SHAPE);  // 80 words needed
+  ERR(f(mk, 5120, tv, 2, -1, 1024, bits, 80, st), DIT_ATTN_ERR_SHAPE);
+  ERR(f(mk, 5120, tv, 2, 1024, 1024, reinterpret_cast<uint64_t*>(FAKE2 + 4), 80, st), DIT_ATTN_ERR_ALIGN);
+  ERR(f(mk, 5120, tv, 70000, 1024, 1024, bits, 80, st), DIT_ATTN_ERR_UNSUPPORTED);
+  OK_LAUNCHES(f(nullptr, 5120, tv, 0, 1024, 1024, bits, 80, st), 0);     // empty: nothing read
+  OK_LAUNCHES(f(nullptr, 0, tv, 2, 1024, 1024, bits, 80, st), 0);
+  OK_LAUNCHES(f(mk, 5120, tv, 2, 1024, 1024, bits, 80, st), 1);
+  expect("key_valid args", g_kv.S == 5120 && g_kv.B == 2 && g_kv.n_text == 1024 && g_kv.bits_stride == 80);
+}
+
+void qknorm_cases() {
+  const int64_t st[3] = {5120LL * 4096, 4096, 128};
+  const int32_t axes[3] = {16, 56, 56};
+  const int32_t* pos = reinterpret_cast<const int32_t*>(FAKE3);
+  auto f = [&](const void* q, int32_t D, const int32_t* ax, int32_t n_axes, int32_t dtype, const int64_t* s,
+               float theta, float eps, int32_t H, int32_t Hk, float q_scale) {
+    return dit_attn_qknorm_rope(q, FAKE, FAKE2, FAKE2 + 0x1000, nullptr, nullptr, 2, 5120, H, Hk, D, s, s, s, s,
+                                pos, n_axes, ax, theta, eps, q_scale, dtype, nullptr);
+  };
+  ERR(f(nullptr, 128, axes, 3, 0, st, 1e4f, 1e-6f, 32, 32, 1.f), DIT_ATTN_ERR_NULL);
+  ERR(f(FAKE, 128, axes, 3, 5, st, 1e4f, 1e-6f, 32, 32, 1.f), DIT_ATTN_ERR_UNSUPPORTED);
+  ERR(f(FAKE, 136, axes, 3, 0, st, 1e4f, 1e-6f, 32, 32, 1.f), DIT_ATTN_ERR_UNSUPPORTED);
+  ERR(f(FAKE, 100, axes, 3, 0, st, 1e4f, 1e-6f, 32, 32, 1.f), DIT_ATTN_ERR_UNSUPPORTED);  // bf16 needs D % 8
+  const int32_t sum126[3] = {16, 56, 54}, odd[3] = {15, 57, 56};
+  ERR(f(FAKE, 128, sum126, 3, 0, st, 1e4f, 1e-6f, 32, 32, 1.f), DIT_ATTN_ERR_SHAPE);
+  ERR(f(FAKE, 128, odd, 3, 0, st, 1e4f, 1e-6f, 32, 32, 1.f), DIT_ATTN_ERR_SHAPE);
+  ERR(f(FAKE, 128, axes, 4, 0, st, 1e4f, 1e-6f, 32, 32, 1.f), DIT_ATTN_ERR_SHAPE);
+  ERR(f(FAKE, 128, axes, 3, 0, st, 0.f, 1e-6f, 32, 32, 1.f), DIT_ATTN_ERR_SHAPE);
+  ERR(f(FAKE, 128, axes, 3, 0, st, kNaN, 1e-6f, 32, 32, 1.f), DIT_ATTN_ERR_SHAPE);
+  ERR(f(FAKE, 128, axes, 3, 0, st, 1e4f, -1.f, 32, 32, 1.f), DIT_ATTN_ERR_SHAPE);
+  ERR(f(FAKE, 128, axes, 3, 0, st, 1e4f, 1e-6f, 32, 32, 0.f), DIT_ATTN_ERR_SHAPE);
+  ERR(f(FAKE, 128, axes, 3, 0, st, 1e4f, 1e-6f, 32, 32, kInf), DIT_ATTN_ERR_SHAPE);
+  ERR(f(FAKE, 128, axes, 3, 0, st, 1e4f, 1e-6f, 0, 32, 1.f), DIT_ATTN_ERR_SHAPE);
+  ERR(f(FAKE + 2, 128, axes, 3, 0, st, 1e4f, 1e-6f, 32, 32, 1.f), DIT_ATTN_ERR_ALIGN);
+  const int64_t bad[3] = {5120LL * 4096, 4096, 132};  // 264-byte head stride
+  ERR(f(FAKE, 128, axes, 3, 0, bad, 1e4f, 1e-6f, 32, 32, 1.f), DIT_ATTN_ERR_ALIGN);
+  const int64_t neg[3] = {5120LL * 4096, -4096, 128};
+  ERR(f(FAKE, 128, axes, 3, 0, neg, 1e4f, 1e-6f, 32, 32, 1.f), DIT_ATTN_ERR_SHAPE);
+  // Accepted: the frequencies of each axis's ladder, in turns per position.
+  OK_LAUNCHES(f(FAKE, 128, axes, 3, 0, st, 1e4f, 1e-6f, 32, 32, 0.5f), 1);
+  bool freq_ok = true;
+  const double two_pi = 6.283185307179586;
+  int p = 0;
+  for (int ax = 0; ax < 3; ++ax)
+    for (int j = 0; j < axes[ax] / 2; ++j, ++p) {
+      const double want = std::pow(1e4, -2.0 * j / axes[ax]) / two_pi;
+      freq_ok = freq_ok && std::fabs(g_norm.omega[p] - want) <= 1e-15 * std::fabs(want) && g_norm.pair_axis[p] == ax;
+    }
+  expect("qknorm frequencies per axis", freq_ok && p == 64);
+  expect("qknorm q_scale", g_norm.q_scale == 0.5f && g_norm.H == 32 && g_norm.Hk == 32 && g_norm.D == 128);
+
+  // The extended entry point.
+  const int64_t st72[3] = {4096LL * 40 * 72, 40 * 72, 72};
+  const int32_t axes2[2] = {36, 36};
+  auto g = [&](const dit_attn_norm_rope_params* prm, int32_t H, int32_t Hk, int32_t D, const void* q, void* qo,
+               int32_t B) {
+    return dit_attn_qknorm_rope_ex(q, FAKE, qo, FAKE2 + 0x1000, B, 4096, H, Hk, D, st72, st72, st72, st72, pos, 2,
+                                   axes2, prm, 0, nullptr);
+  };
+  dit_attn_norm_rope_params pr = params(DIT_ATTN_NORM_LAYER_ACROSS_HEADS);
+  ERR(g(nullptr, 32, 8, 72, FAKE, FAKE2, 2), DIT_ATTN_ERR_NULL);
+  ERR(g(&pr, 32, 8, 72, nullptr, FAKE2, 2), DIT_ATTN_ERR_NULL);   // q_out without q
+  ERR(g(&pr, 32, 8, 72, FAKE, nullptr, 2), DIT_ATTN_ERR_NULL);    // q without q_out
+  dit_attn_norm_rope_params x = pr;
+  x.norm = 2;
+  ERR(g(&x, 32, 8, 72, FAKE, FAKE2, 2), DIT_ATTN_ERR_UNSUPPORTED);
+  x = pr;
+  x.rope_linear_factor = 0.f;
+  ERR(g(&x, 32, 8, 72, FAKE, FAKE2, 2), DIT_ATTN_ERR_SHAPE);
+  x = pr;
+  x.rope_ntk_factor = kInf;
+  ERR(g(&x, 32, 8, 72, FAKE, FAKE2, 2), DIT_ATTN_ERR_SHAPE);
+  x = pr;
+  x.eps = kNaN;
+  ERR(g(&x, 32, 8, 72, FAKE, FAKE2, 2), DIT_ATTN_ERR_SHAPE);
+  x = pr;
+  x.q_bias = FAKE + 4;
+  ERR(g(&x, 32, 8, 72, FAKE, FAKE2, 2), DIT_ATTN_ERR_ALIGN);
+  ERR(g(&pr, 256, 256, 128, FAKE, FAKE2, 2), DIT_ATTN_ERR_UNSUPPORTED);  // (256 + 256) * 16 items > 2048
+  OK_LAUNCHES(g(&pr, 32, 8, 72, nullptr, nullptr, 0), 0);                // empty: nothing read
+  // K alone with the rotary factors folded into the frequencies.
+  x = params();
+  x.rope_linear_factor = 2.f;
+  x.rope_ntk_factor = 4.f;
+  OK_LAUNCHES(g(&x, 0, 8, 72, nullptr, nullptr, 2), 1);
+  const double want1 = std::pow(4e4, -2.0 / 36) / 2.0 / two_pi;  // pair 1 of the first axis
+  expect("qknorm_ex K only", g_norm.H == 0 && g_norm.q == nullptr && g_norm.qo == nullptr);
+  expect("qknorm_ex folded factors", std::fabs(g_norm.omega[1] - want1) <= 1e-15 * want1);
+}
+
+void attention_cases() {
+  const int64_t s[3] = {5120LL * 4096, 4096, 128};
+  const int64_t st4[4][3] = {{s[0], s[1], s[2]}, {s[0], s[1], s[2]}, {s[0], s[1], s[2]}, {s[0], s[1], s[2]}};
+  dit_attn_token_meta m = meta_of(5120);
+  auto f = [&](const void* q, int32_t S, int32_t H, int32_t Hk, int32_t D, int32_t mask,
+               const dit_attn_token_meta* mp, int32_t dtype, float* lse) {
+    return dit_attn_forward(q, FAKE, FAKE + 0x1000, FAKE2, lse, 2, S, H, Hk, D, st4, mask, mp, 0.f, dtype, nullptr);
+  };
+  ERR(f(nullptr, 5120, 32, 32, 128, 1, &m, 0, nullptr), DIT_ATTN_ERR_NULL);
+  ERR(f(FAKE, 5120, 32, 32, 128, 1, nullptr, 0, nullptr), DIT_ATTN_ERR_NULL);  // block-causal needs kv_limit
+  ERR(f(FAKE, 5000, 32, 32, 128, 1, &m, 0, nullptr), DIT_ATTN_ERR_SHAPE);      // metadata length
+  ERR(f(FAKE, 5120, 32, 5, 128, 1, &m, 0, nullptr), DIT_ATTN_ERR_SHAPE);       // 32 % 5
+  ERR(f(FAKE, 5120, 32, 32, 256, 1, &m, 0, nullptr), DIT_ATTN_ERR_UNSUPPORTED);
+  ERR(f(FAKE, 5120, 32, 32, 128, 3, &m, 0, nullptr), DIT_ATTN_ERR_UNSUPPORTED);
+  ERR(f(FAKE, 5120, 32, 32, 128, 1, &m, 2, nullptr), DIT_ATTN_ERR_UNSUPPORTED);
+  ERR(f(FAKE + 8, 5120, 32, 32, 128, 1, &m, 0, nullptr), DIT_ATTN_ERR_ALIGN);
+  OK_LAUNCHES(dit_attn_forward(nullptr, nullptr, nullptr, nullptr, nullptr, 0, 16, 32, 32, 128, st4, 0, nullptr,
+                               0.f, 0, nullptr),
+              0);
+  OK_LAUNCHES(dit_attn_forward(nullptr, nullptr, nullptr, nullptr, nullptr, 2, 0, 32, 32, 128, st4, 0, nullptr,
+                               0.f, 0, nullptr),
+              0);
+  // Accepted: no cache, the default scale 1/sqrt(D), every pointer passed on.
+  float* lse = reinterpret_cast<float*>(FAKE3);
+  OK_LAUNCHES(f(FAKE, 5120, 32, 32, 128, 1, &m, 0, lse), 1);
+  expect("attn pointers", g_attn.q == FAKE && g_attn.kn == FAKE && g_attn.vn == FAKE + 0x1000 &&
+                              g_attn.o == FAKE2 && g_attn.lse == lse && g_attn.kv_limit == m.kv_limit);
+  expect("attn sizes", g_attn.P == 0 && g_attn.Snew == 5120 && g_attn.Sk == 5120 && g_attn.key_bits == nullptr);
+  expect("attn default scale", std::fabs(g_attn.scale - 1.f / std::sqrt(128.f)) < 1e-7f && g_attn.qpos == nullptr);
+  OK_LAUNCHES(f(FAKE, 5120, 32, 8, 72, 0, nullptr, 0, nullptr), 1);  // full mask needs no metadata
+  expect("attn full mask", g_attn.kv_limit == nullptr && g_attn.Hk == 8 && g_attn.D == 72);
+
+  // Cached form.
+  const int64_t st6[6][3] = {{s[0], s[1], s[2]}, {s[0], s[1], s[2]}, {s[0], s[1], s[2]},
+                             {s[0], s[1], s[2]}, {s[0], s[1], s[2]}, {s[0], s[1], s[2]}};
+  dit_attn_token_meta m116 = meta_of(116), m100 = meta_of(100);
+  ERR(dit_attn_forward_cached(FAKE, nullptr, nullptr, FAKE, FAKE, FAKE2, nullptr, 1, 16, 100, 32, 32, 128, st6, 1,
+                              &m116, 0.f, 0, nullptr),
+      DIT_ATTN_ERR_NULL);  // P > 0 needs the cache
+  ERR(dit_attn_forward_cached(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE2, nullptr, 1, 16, 100, 32, 32, 128, st6, 1, &m100,
+                              0.f, 0, nullptr),
+      DIT_ATTN_ERR_SHAPE);  // seq_len must be P + S_new
+  OK_LAUNCHES(dit_attn_forward_cached(FAKE, FAKE3, FAKE3 + 0x1000, FAKE, FAKE + 0x1000, FAKE2, nullptr, 1, 16, 100,
+                                      32, 32, 128, st6, 1, &m116, 0.25f, 0, nullptr),
+              1);
+  expect("cached pointers", g_attn.kc == FAKE3 && g_attn.vc == FAKE3 + 0x1000 && g_attn.P == 16 &&
+                                g_attn.Snew == 100 && g_attn.Sk == 116 && g_attn.scale == 0.25f);
+
+  // Padded forms.
+  const uint64_t* kb = reinterpret_cast<const uint64_t*>(FAKE2 + 0x100000);
+  auto fp = [&](const void* q, const uint64_t* bits, int64_t words, int32_t S, int32_t B,
+                const dit_attn_token_meta* mp) {
+    return dit_attn_forward_padded(q, FAKE, FAKE, FAKE2, nullptr, B, S, 32, 32, 128, st4, 1, mp, bits, words, 0.f, 0,
+                                   nullptr);
+  };
+  ERR(fp(FAKE, nullptr, 80, 5120, 2, &m), DIT_ATTN_ERR_NULL);
+  ERR(fp(nullptr, kb, 80, 5120, 2, &m), DIT_ATTN_ERR_NULL);
+  ERR(fp(FAKE, kb, 79, 5120, 2, &m), DIT_ATTN_ERR_SHAPE);
+  ERR(fp(FAKE, reinterpret_cast<const uint64_t*>(FAKE2 + 4), 80, 5120, 2, &m), DIT_ATTN_ERR_ALIGN);
+  ERR(fp(FAKE, kb, 80, 5000, 2, &m), DIT_ATTN_ERR_SHAPE);
+  OK_LAUNCHES(fp(nullptr, kb, 80, 5120, 0, &m), 0);
+  OK_LAUNCHES(fp(FAKE, kb, 80, 5120, 2, &m), 1);
+  expect("padded bits", g_attn.key_bits == kb && g_attn.kb_stride == 80);
+  ERR(dit_attn_forward_cached_padded(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE2, nullptr, 1, 16, 100, 32, 32, 128, st6, 1,
+                                     &m116, kb, 1, 0.f, 0, nullptr),
+      DIT_ATTN_ERR_SHAPE);  // 116 logical keys need 2 words
+  ERR(dit_attn_forward_cached_padded(FAKE, nullptr, FAKE, FAKE, FAKE, FAKE2, nullptr, 1, 16, 100, 32, 32, 128, st6,
+                                     1, &m116, kb, 2, 0.f, 0, nullptr),
+      DIT_ATTN_ERR_NULL);
+}
+
+void fused_cases() {
+  const int64_t s[3] = {4096LL * 4096, 4096, 128};
+  const int64_t st6[6][3] = {{s[0], s[1], s[2]}, {s[0], s[1], s[2]}, {s[0], s[1], s[2]},
+                             {s[0], s[1], s[2]}, {s[0], s[1], s[2]}, {s[0], s[1], s[2]}};
+  const int32_t axes[3] = {16, 56, 56};
+  const int32_t* pos = reinterpret_cast<const int32_t*>(FAKE2 + 0x10000);
+  auto f = [&](const void* q, const void* kc, int32_t P, const uint64_t* kb, int64_t words, const int32_t* ps,
+               const int32_t* ax, int32_t n_axes, const dit_attn_norm_rope_params* prm, int32_t dtype, int32_t B,
+               int32_t S, int32_t D) {
+    dit_attn_token_meta m = meta_of(P + S);
+    return dit_attn_forward_cached_qnorm(q, kc, FAKE, FAKE, FAKE, FAKE2, nullptr, B, P, S, 32, 32, D, st6, 1, &m, kb,
+                                         words, ps, n_axes, ax, prm, 0.f, dtype, nullptr);
+  };
+  dit_attn_norm_rope_params p = params();
+  ERR(f(FAKE, FAKE, 16, nullptr, 0, nullptr, axes, 3, &p, 0, 1, 100, 128), DIT_ATTN_ERR_NULL);
+  ERR(f(FAKE, FAKE, 16, nullptr, 0, pos, axes, 3, nullptr, 0, 1, 100, 128), DIT_ATTN_ERR_NULL);
+  ERR(f(nullptr, FAKE, 16, nullptr, 0, pos, axes, 3, &p, 0, 1, 100, 128), DIT_ATTN_ERR_NULL);
+  ERR(f(FAKE, nullptr, 16, nullptr, 0, pos, axes, 3, &p, 0, 1, 100, 128), DIT_ATTN_ERR_NULL);
+  ERR(f(FAKE, FAKE, 16, nullptr, 0, pos, axes, 3, &p, 1, 1, 100, 128), DIT_ATTN_ERR_UNSUPPORTED);  // bf16 only
+  dit_attn_norm_rope_params x = params(DIT_ATTN_NORM_LAYER_ACROSS_HEADS);
+  ERR(f(FAKE, FAKE, 16, nullptr, 0, pos, axes, 3, &x, 0, 1, 100, 128), DIT_ATTN_ERR_UNSUPPORTED);
+  const int32_t ax136[3] = {16, 56, 64}, ax130[3] = {16, 56, 58}, axodd[3] = {17, 55, 56};
+  ERR(f(FAKE, FAKE, 16, nullptr, 0, pos, ax136, 3, &p, 0, 1, 100, 136), DIT_ATTN_ERR_UNSUPPORTED);
+  ERR(f(FAKE, FAKE, 16, nullptr, 0, pos, ax130, 3, &p, 0, 1, 100, 128), DIT_ATTN_ERR_SHAPE);
+  ERR(f(FAKE, FAKE, 16, nullptr, 0, pos, axodd, 3, &p, 0, 1, 100, 128), DIT_ATTN_ERR_SHAPE);
+  for (int which = 0; which < 6; ++which) {
+    x = params();
+    if (which == 0) x.rope_ntk_factor = 0.f;
+    if (which == 1) x.rope_linear_factor = kInf;
+    if (which == 2) x.rope_theta = -1.f;
+    if (which == 3) x.eps = -1.f;
+    if (which == 4) x.eps = kNaN;
+    if (which == 5) x.q_scale = 0.f;
+    ERR(f(FAKE, FAKE, 16, nullptr, 0, pos, axes, 3, &x, 0, 1, 100, 128), DIT_ATTN_ERR_SHAPE);
+  }
+  x = params();
+  x.q_weight = FAKE + 2;
+  ERR(f(FAKE, FAKE, 16, nullptr, 0, pos, axes, 3, &x, 0, 1, 100, 128), DIT_ATTN_ERR_ALIGN);
+  ERR(f(FAKE, FAKE, 16, nullptr, 0, reinterpret_cast<const int32_t*>(FAKE2 + 2), axes, 3, &p, 0, 1, 100, 128),
+      DIT_ATTN_ERR_ALIGN);
+  const uint64_t* kb = reinterpret_cast<const uint64_t*>(FAKE3);
+  ERR(f(FAKE, FAKE, 16, kb, 1, pos, axes, 3, &p, 0, 1, 100, 128), DIT_ATTN_ERR_SHAPE);  // 116 keys: 2 words
+  OK_LAUNCHES(f(nullptr, FAKE, 16, nullptr, 0, nullptr, axes, 3, &p, 0, 0, 100, 128), 0);
+  OK_LAUNCHES(f(nullptr, FAKE, 16, nullptr, 0, pos, axes, 3, &p, 0, 1, 0, 128), 0);
+  // Accepted: the softmax scale and log2(e) go into Q with its norm (scale
+  // argument ln 2), and each pair's frequency is set under its own axis only.
+  x = params();
+  x.q_scale = 2.f;
+  x.q_weight = FAKE3 + 0x100;
+  OK_LAUNCHES(f(FAKE, FAKE, 16, kb, 2, pos, axes, 3, &x, 0, 1, 100, 128), 1);
+  const double want_qs = 2.0 / std::sqrt(128.0) * 1.4426950408889634;
+  expect("fused q_scale", std::fabs(g_attn.q_scale - want_qs) <= 1e-6 * want_qs);
+  expect("fused ln2 scale", g_attn.scale == 0.6931471805599453f);
+  expect("fused q pointers", g_attn.qpos == pos && g_attn.wq == FAKE3 + 0x100 && g_attn.eps == 1e-6f);
+  bool axis_ok = true;
+  int pr = 0;
+  for (int ax = 0; ax < 3; ++ax)
+    for (int j = 0; j < axes[ax] / 2; ++j, ++pr)
+      for (int a2 = 0; a2 < 3; ++a2) {
+        const double want = a2 == ax ? std::pow(1e4, -2.0 * j / axes[ax]) / 6.283185307179586 : 0.0;
+        axis_ok = axis_ok && std::fabs(g_attn.omega_axis[a2][pr] - want) <= 1e-15 * std::fabs(want);
+      }
+  expect("fused per-axis frequencies", axis_ok);
+}
+
+void cfg_cases() {
+  auto f = [&](const void* c, const void* u, void* o, int64_t rows, int32_t C, int64_t cs, int64_t us, int64_t os,
+               float g, int32_t dtype) { return dit_attn_cfg_norm_rescale(c, u, o, rows, C, cs, us, os, g, dtype, nullptr); };
+  ERR(f(nullptr, FAKE2, FAKE2, 4096, 64, 64, 64, 64, 4.f, 0), DIT_ATTN_ERR_NULL);
+  ERR(f(FAKE, FAKE2, FAKE2, 4096, 60, 64, 64, 64, 4.f, 0), DIT_ATTN_ERR_UNSUPPORTED);
+  ERR(f(FAKE, FAKE2, FAKE2, 4096, 8 * 513, 8 * 513, 8 * 513, 8 * 513, 4.f, 0), DIT_ATTN_ERR_UNSUPPORTED);
+  ERR(f(FAKE, FAKE2, FAKE2, 4096, 64, 32, 64, 64, 4.f, 0), DIT_ATTN_ERR_SHAPE);
+  ERR(f(FAKE, FAKE2, FAKE2, 4096, 64, 64, 64, 64, kNaN, 0), DIT_ATTN_ERR_SHAPE);
+  ERR(f(FAKE, FAKE2, FAKE2, 4096, 0, 64, 64, 64, 4.f, 0), DIT_ATTN_ERR_SHAPE);
+  ERR(f(FAKE, FAKE2, FAKE2, 4096, 64, 64, 64, 64, 4.f, 3), DIT_ATTN_ERR_UNSUPPORTED);
+  ERR(f(FAKE, FAKE2 + 8, FAKE2, 4096, 64, 64, 64, 64, 4.f, 0), DIT_ATTN_ERR_ALIGN);
+  ERR(f(FAKE, FAKE2, FAKE2, 4096, 64, 68, 64, 64, 4.f, 0), DIT_ATTN_ERR_ALIGN);
+  OK_LAUNCHES(f(nullptr, FAKE2, FAKE2, 0, 64, 64, 64, 64, 4.f, 0), 0);
+  OK_LAUNCHES(f(FAKE, FAKE2, FAKE3, 131072, 64, 64, 64, 64, 4.f, 0), 1);
+  expect("cfg args", g_cfg.rows == 131072 && g_cfg.C == 64 && g_cfg.g == 4.f && g_cfg.out == FAKE3);
+}
+
+void host_helper_cases() {
+  float lin = 0.f, ntk = 0.f;
+  expect("factors before the watershed",
+         dit_attn_time_aware_rope_factors(0.1f, 0.3f, 2.f, &lin, &ntk) == 0 && lin == 2.f && ntk == 1.f);
+  expect("factors from the watershed on",
+         dit_attn_time_aware_rope_factors(0.3f, 0.3f, 2.f, &lin, &ntk) == 0 && lin == 1.f && ntk == 2.f);
+  ERR(dit_attn_time_aware_rope_factors(0.1f, 0.3f, 2.f, nullptr, &ntk), DIT_ATTN_ERR_NULL);
+  ERR(dit_attn_time_aware_rope_factors(kNaN, 0.3f, 2.f, &lin, &ntk), DIT_ATTN_ERR_SHAPE);
+  ERR(dit_attn_time_aware_rope_factors(0.1f, 0.3f, 0.f, &lin, &ntk), DIT_ATTN_ERR_SHAPE);
+  float qs = 0.f;
+  expect("prescaled factor default", dit_attn_prescaled_q_factor(128, 0.f, &qs) == 0 &&
+                                         qs == (float)(1.4426950408889634 / std::sqrt(128.0)));
+  expect("prescaled factor explicit", dit_attn_prescaled_q_factor(72, 0.5f, &qs) == 0 &&
+                                          qs == (float)(0.5 * 1.4426950408889634));
+  ERR(dit_attn_prescaled_q_factor(128, 0.f, nullptr), DIT_ATTN_ERR_NULL);
+  ERR(dit_attn_prescaled_q_factor(0, 0.f, &qs), DIT_ATTN_ERR_SHAPE);
+  ERR(dit_attn_prescaled_q_factor(128, kInf, &qs), DIT_ATTN_ERR_SHAPE);
+  for (int st = -1; st <= 7; ++st) expect("status string", dit_attn_status_string(st) != nullptr);
+  expect("unknown status", std::strcmp(dit_attn_status_string(99), "unknown status") == 0);
+}
+}  // namespace
+
+int main() {
+  metadata_cases();
+  key_valid_cases();
+  qknorm_cases();
+  attention_cases();
+  fused_cases();
+  cfg_cases();
+  host_helper_cases();
+  if (g_failed) {
+    std::printf("hostcheck: %d of %d cases failed\n", g_failed, g_cases);
+    return 1;
+  }
+  std::printf("hostcheck: %d cases passed\n", g_cases);
+  return 0;
+}

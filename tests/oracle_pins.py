@@ -18,6 +18,7 @@ import oracle.attention as att
 import oracle.cfg as ocfg
 import oracle.key_padding as kp
 import oracle.metadata as meta
+import oracle.pipeline as pipe
 import oracle.qknorm_rope as qr
 from tests import goldens
 from workloads import Workload, sequence_inputs, small_workload
@@ -509,10 +510,59 @@ def pin_key_padding_bruteforce_and_empty_rows():
     assert np.all(np.isfinite(lse[0, :, 2:])) and np.all(np.isfinite(lse[1]))
 
 
+# --------------------------------------------------------------------------- the composed step
+def pin_pipeline_step():
+    """The composed step (oracle.pipeline).
+    1. Text only, no cache: O equals causal torch SDPA (float64, CPU) over the
+       normed and rotated Q and K at the metadata's positions, and the query
+       rows asked for equal the same rows of the whole output.
+    2. The "extract" then "cached" flow (QwenImage21Transformer2DModel API
+       page, forward's kv_cache modes; the causal_condition note): on a
+       layout [text, condition image, text, target image] the full step's
+       target rows equal a cached step over the target tokens alone whose
+       cache is rows [0, P) of the full step's K' and raw V, for O, lse and
+       the target tokens' K'; with padded text keys too."""
+    rng = np.random.default_rng(31)
+    axes = (4, 6, 6)
+    D = sum(axes)
+    mask, shapes = _layout_inputs((("T", 11),))
+    md = meta.build_token_metadata(mask, shapes)
+    S = len(mask)
+    vals = {"q": rng.standard_normal((2, S, 4, D)), "k": rng.standard_normal((2, S, 2, D)),
+            "v": rng.standard_normal((2, S, 2, D)), "wq": 1 + 0.1 * rng.standard_normal(D),
+            "wk": 1 + 0.1 * rng.standard_normal(D)}
+    out = pipe.step(vals, md, axes=axes, eps=1e-6, mask_mode="block_causal")
+    qp = qr.qknorm_rope(vals["q"], vals["wq"], 1e-6, md["pos_ids"], axes)
+    kp_ = qr.qknorm_rope(vals["k"], vals["wk"], 1e-6, md["pos_ids"], axes)
+    ke = torch.repeat_interleave(torch.from_numpy(kp_), 2, dim=2).numpy()
+    ve = torch.repeat_interleave(torch.from_numpy(vals["v"]), 2, dim=2).numpy()
+    assert np.allclose(out["o"], _sdpa(qp, ke, ve, is_causal=True), rtol=1e-10, atol=1e-12)
+    sub = pipe.step(vals, md, axes=axes, eps=1e-6, mask_mode="block_causal", rows=[0, 5, 10])
+    assert np.allclose(sub["o"], out["o"][:, [0, 5, 10]], rtol=1e-12, atol=1e-14)
+
+    layout = (("T", 5), ("I", 1, 2, 2), ("T", 3), ("I", 1, 2, 4))
+    mask, shapes = _layout_inputs(layout)
+    md = meta.build_token_metadata(mask, shapes)
+    S, P = len(mask), 12
+    vals = {"q": rng.standard_normal((2, S, 4, D)), "k": rng.standard_normal((2, S, 2, D)),
+            "v": rng.standard_normal((2, S, 2, D)), "wq": 1 + 0.1 * rng.standard_normal(D),
+            "wk": 1 + 0.1 * rng.standard_normal(D)}
+    tv = np.array([[1, 1, 0, 1, 1, 0, 1, 1], [1, 0, 1, 1, 1, 1, 1, 0]], bool)
+    for key_valid in (None, kp.joint_key_valid(mask, tv)):
+        full = pipe.step(vals, md, axes=axes, eps=1e-6, mask_mode="block_causal", key_valid=key_valid)
+        new = {n: vals[n][:, P:] for n in ("q", "k", "v")}
+        new.update(wq=vals["wq"], wk=vals["wk"], **pipe.extract_cache(full, vals["v"], P))
+        cached = pipe.step(new, md, axes=axes, eps=1e-6, mask_mode="block_causal", prefix_len=P,
+                           key_valid=key_valid)
+        assert np.allclose(cached["o"], full["o"][:, P:], rtol=1e-12, atol=1e-14)
+        assert np.allclose(cached["lse"], full["lse"][:, :, P:], rtol=1e-12, atol=1e-14)
+        assert np.allclose(cached["k_prime"], full["k_prime"][:, P:], rtol=1e-12, atol=1e-14)
+
+
 ALL_PINS = [pin_metadata_goldens, pin_kv_limit_is_predicate_prefix, pin_metadata_errors,
             pin_rmsnorm_closed_forms, pin_rope_rotation, pin_rope_pairing_and_ladder, pin_rope_relative,
             pin_full_is_sdpa, pin_text_only_is_causal, pin_gqa_is_repeat_interleave,
             pin_singlepass_equals_multipass, pin_adjacent_blocks_stay_separate, pin_cached_equals_full,
             pin_bruteforce_tiny, pin_lse_definition, pin_key_padding_fixtures, pin_key_padding_is_masked_sdpa,
             pin_key_padding_is_compaction, pin_key_padding_bruteforce_and_empty_rows, pin_layernorm_across_heads,
-            pin_scaled_rope, pin_time_aware_factors, pin_cfg_norm_rescale]
+            pin_scaled_rope, pin_time_aware_factors, pin_cfg_norm_rescale, pin_pipeline_step]

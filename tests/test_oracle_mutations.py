@@ -7,6 +7,7 @@ import oracle.attention as att
 import oracle.cfg as ocfg
 import oracle.key_padding as kp
 import oracle.metadata as meta
+import oracle.pipeline as opipe
 import oracle.qknorm_rope as qr
 from tests import oracle_pins as pins
 
@@ -232,6 +233,33 @@ def _metadata_uncentred(image_pad_mask, img_shapes, pos_mode="centered_fhw"):
     return md
 
 
+pipe_step_orig = opipe.step
+
+
+def _pipeline_positions_from_start(vals, md, **kw):
+    # Mistake: the new tokens take the rotary positions of the first S_new
+    # tokens of the sequence instead of their own, [P, P + S_new).
+    P, S_new = kw.get("prefix_len", 0), np.asarray(vals["q"]).shape[1]
+    md2 = dict(md)
+    pos = np.array(md["pos_ids"], copy=True)
+    pos[P:P + S_new] = md["pos_ids"][:S_new]
+    md2["pos_ids"] = pos
+    return pipe_step_orig(vals, md2, **kw)
+
+
+def _pipeline_cached_rows_without_offset(vals, md, **kw):
+    # Mistake: the cached step's attention called without the prefix offset,
+    # so its query rows take the key bounds of the sequence's first tokens.
+    out = pipe_step_orig(vals, md, **kw)
+    if kw.get("prefix_len", 0) == 0:
+        return out
+    k_all = np.concatenate([vals["k_cache"], out["k_prime"]], axis=1)
+    v_all = np.concatenate([vals["v_cache"], vals["v"]], axis=1)
+    o, lse = att.attention(out["q_prime"], k_all, v_all, md["image_ids"], kw["mask_mode"], rows=kw.get("rows"),
+                           key_valid=kw.get("key_valid"))
+    out.update(o=o, lse=lse)
+    return out
+
 def _wrap_allowed(fn):
     orig = att.allowed_matrix
 
@@ -267,6 +295,8 @@ MUTATIONS = [
     ("cfg_without_rescale", ocfg, "norm_rescaled_cfg", _cfg_no_rescale),
     ("cfg_rescaled_to_uncond_norm", ocfg, "norm_rescaled_cfg", _cfg_rescale_to_uncond),
     ("cfg_mix_direction_swapped", ocfg, "norm_rescaled_cfg", _cfg_swapped_mix),
+    ("pipeline_positions_from_sequence_start", opipe, "step", _pipeline_positions_from_start),
+    ("pipeline_cached_rows_without_offset", opipe, "step", _pipeline_cached_rows_without_offset),
 ]
 
 
