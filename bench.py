@@ -73,6 +73,64 @@ def text_valid_keys(mask: np.ndarray, tv: np.ndarray) -> np.ndarray:
     return out
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (Linux /proc/cpuinfo), or "" if unknown."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
+
+
+_SMI = {}
+
+
+def read_clocks() -> dict:
+    """Current shader clock of each XCD and memory clock of GPU 0, in MHz, and
+    the socket power in W, read in-process through the amdsmi library (the
+    data `amd-smi metric` shows), or {"error": ...}."""
+    try:
+        import amdsmi
+        if "handle" not in _SMI:
+            amdsmi.amdsmi_init()
+            _SMI["handle"] = amdsmi.amdsmi_get_processor_handles()[0]
+        m = amdsmi.amdsmi_get_gpu_metrics_info(_SMI["handle"])
+    except Exception as e:  # noqa: BLE001  (no amdsmi, no device, no permission)
+        return {"error": "%s: %s" % (type(e).__name__, e)}
+
+    def mhz(v):
+        vals = v if isinstance(v, (list, tuple)) else [v]
+        return [int(x) for x in vals if isinstance(x, (int, float)) and 0 < x < 65535]
+    out = {"sclk_mhz": mhz(m.get("current_gfxclks", [])), "mclk_mhz": mhz(m.get("current_uclk", []))}
+    p = m.get("current_socket_power")
+    if isinstance(p, (int, float)) and 0 < p < 65535:
+        out["socket_power_w"] = p
+    return out
+
+
+def clocks_under_load(torch, run, seconds: float = 1.5) -> dict:
+    """Run `run()` back to back for `seconds` while another thread reads the
+    clocks once, half-way through: the clocks the timed steps ran at."""
+    import threading
+    box = {}
+
+    def probe():
+        time.sleep(seconds / 2)
+        box.update(read_clocks())
+    th = threading.Thread(target=probe)
+    t0 = time.perf_counter()
+    th.start()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            run()
+        torch.cuda.synchronize()
+    th.join()
+    return box
+
+
 def source_sha(path: str) -> str:
     with open(path, "rb") as fh:
         return hashlib.sha256(fh.read()).hexdigest()
@@ -321,6 +379,77 @@ def multistep(step: Step, n_steps: int, reps: int, warmup: int, full_ms: float, 
             "cached_rows_equal_full_rows": same}
 
 
+OTHER_CONFIGS = ("lumina_next_full_gqa", "cond_images_t256_2x32x32_t256_i64x64", "cached_prefix_decode_i128x128")
+
+
+def measure_config(name: str, steps: int, warmup: int, ramp_s: float) -> dict:
+    """Step and attention-kernel times of one more bf16 workload, measured the
+    way the headline is (time_gpu), for the line's `configs` object."""
+    import torch
+    w = wl.get(name)
+    step = Step(w, "cuda")
+    step.run()
+    torch.cuda.synchronize()
+    step.meta.check()
+    pairs = useful_pairs(step.meta.kv_limit.cpu().numpy(), w)
+    flops = 4.0 * w.head_dim * pairs * w.heads
+    t = time_gpu(step, steps, warmup, ramp_s)
+    attn = flops / (t["attn_ms_mean"] * 1e-3) / 1e12
+    elem = 2 if w.dtype == "bf16" else 4
+    normed = w.kv_heads if step.fused else w.heads + w.kv_heads
+    norm_bytes = 2 * w.batch * w.n_new * normed * w.head_dim * elem
+    out = {"workload": name, "batch": w.batch, "heads": w.heads, "kv_heads": w.kv_heads, "head_dim": w.head_dim,
+           "seq_len": w.seq_len, "queries": w.n_new, "mask": w.mask_mode, "flops_per_step": flops,
+           "step_ms": t["step_ms"], "step_tflops": flops / (t["step_ms"] * 1e-3) / 1e12,
+           "attention_ms_mean": t["attn_ms_mean"], "attention_ms_min": t["attn_ms_min"],
+           "attention_tflops": attn, "attention_frac_bf16_peak": attn / PEAK_BF16_TFLOPS,
+           "qknorm_rope_ms": t["norm_ms"], "qknorm_rope_frac_hbm": norm_bytes / (t["norm_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+           "token_metadata_ms": t["meta_ms"],
+           "kernel": "attn_fwd_bf16_kernel<%d,4%s>" % (80 if 64 < w.head_dim <= 80 else (w.head_dim + 31) // 32 * 32,
+                                                       ",qnorm" if step.fused else "")}
+    del step
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_single_thread() -> dict:
+    """The oracle on one host thread for the tiny fp32 workload (every query
+    row) and the Lumina mini shape of the Lumina-Next article's standalone
+    test (3 query heads over 1 KV head, head_dim 8, 2D rotary 4 + 4 on a 4x4
+    grid, full mask): seconds and fp64 useful GFLOP/s."""
+    import oracle.attention as oatt
+    import oracle.metadata as ometa
+    import oracle.qknorm_rope as oqr
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # noqa: BLE001
+        threadpool_limits = None
+    cases = [wl.get("tiny_f32_block_causal"),
+             wl.small_workload("lumina_mini", 1, 3, 1, 8, (("I", 1, 4, 4),), (4, 4), pos_mode="grid_hw",
+                               mask_mode="full", dtype="f32", seed=0)]
+    out = {}
+    import contextlib
+    ctx = threadpool_limits(1) if threadpool_limits else contextlib.nullcontext()
+    with ctx:
+        for w in cases:
+            d = wl.draw(w)
+            mask, shapes = wl.sequence_inputs(w)
+            reps, t0 = 0, time.perf_counter()
+            while time.perf_counter() - t0 < 0.5:
+                md = ometa.build_token_metadata(mask, shapes, w.pos_mode)
+                qp = oqr.qknorm_rope(d.vals["q"], d.vals["wq"], w.eps, md["pos_ids"], w.axes)
+                kp = oqr.qknorm_rope(d.vals["k"], d.vals["wk"], w.eps, md["pos_ids"], w.axes)
+                oatt.attention(qp, kp, d.vals["v"], md["image_ids"], w.mask_mode)
+                reps += 1
+            el = (time.perf_counter() - t0) / reps
+            lim = (np.full(w.n_new, w.seq_len) if w.mask_mode == "full"
+                   else ometa.build_token_metadata(mask, shapes, w.pos_mode)["kv_limit"])
+            flops = 4.0 * w.head_dim * int(np.sum(lim)) * w.batch * w.heads
+            out[w.name] = {"seconds_per_step": el, "gflops": flops / el / 1e9, "threads": 1,
+                           "step": "metadata + norm/rope of Q and K + attention, all rows"}
+    return out
+
+
 def cpu_baseline(w: wl.Workload, drawn: wl.Drawn, budget_s: float = 12.0, text_valid=None):
     """The fp64 oracle (as it stands) on the host: norm + rope of the sampled
     query rows, then their attention rows; rows drawn at random from the
@@ -363,8 +492,9 @@ def cpu_baseline(w: wl.Workload, drawn: wl.Drawn, budget_s: float = 12.0, text_v
     elapsed = time.perf_counter() - t0
     flops = 4.0 * w.head_dim * pairs * w.heads
     return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": "%d random query rows (all %d heads x batch %d) of %s incl. K norm+rope of every token; "
-                      "%.1f s wall" % (rows_done, w.heads, w.batch, w.name, elapsed),
+            "sample": "%d random query rows (all %d heads x batch %d) of %s, each row's attention computed on "
+                      "its own (one oracle call per row), incl. K norm+rope of every token; %.1f s wall; BLAS "
+                      "threads %d" % (rows_done, w.heads, w.batch, w.name, elapsed, threads),
             "seconds": elapsed}
 
 
@@ -545,6 +675,8 @@ def main(argv=None) -> int:
                     help="two-kernel form: the norm kernel writes Q' and the attention reads it (default for bf16 "
                          "with the per-head RMSNorm: Q's norm and rotation inside the attention kernel)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the step and attention timings of the other bf16 workloads (the line's `configs`)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (the reference "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -581,6 +713,7 @@ def main(argv=None) -> int:
         log("copied %d bytes five times" % n)
         return 0
 
+    clocks_before = read_clocks()
     w = wl.get(args.workload)
     if args.shard_heads > 1:
         K = args.shard_heads
@@ -612,6 +745,8 @@ def main(argv=None) -> int:
 
     t = time_gpu(step, args.steps, args.warmup, args.clock_ramp_s)
     log("timing: %s" % json.dumps(t))
+    clocks_load = clocks_under_load(torch, step.run)
+    log("clocks under load: %s" % json.dumps(clocks_load))
     cold = time_norm_cold(step, ramp_s=args.clock_ramp_s)
     log("norm/rope with rotated inputs: %s" % json.dumps(cold))
     props = torch.cuda.get_device_properties(0)
@@ -663,6 +798,16 @@ def main(argv=None) -> int:
         line["config"]["text_padding"] = {"kind": args.text_padding, "text_tokens": int(step.tv.shape[1]),
                                           "valid_per_sample": step.tv.sum(axis=1).tolist()}
         line["config"]["step"] = "token metadata + key validity + qk-rmsnorm/rope + padded attention"
+    other = (not args.no_other_configs and args.workload == DEFAULT_WORKLOAD and args.shard_heads == 1
+             and args.text_padding == "none" and not args.unfused_q)
+    if other:
+        line["configs"] = {}
+        for name in OTHER_CONFIGS:
+            c = measure_config(name, args.steps, args.warmup, args.clock_ramp_s)
+            log("config %s: %s" % (name, json.dumps(c)))
+            line["configs"][name] = c
+    line["clocks"] = {"before": clocks_before, "under_load": clocks_load, "after": read_clocks()}
+    line["host"] = {"cpu_model": cpu_model(), "cores": len(os.sched_getaffinity(0))}
     if args.multistep:
         ms = multistep(step, args.multistep, args.steps, args.warmup, t["step_ms"], args.clock_ramp_s)
         log("multistep: %s" % json.dumps(ms))
@@ -671,6 +816,7 @@ def main(argv=None) -> int:
         log("cpu baseline: oracle on host cores, ~%.0f s" % args.cpu_budget)
         cb = cpu_baseline(w, step.drawn, args.cpu_budget, step.tv)
         line["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
+        line["cpu_baseline"]["single_thread"] = cpu_single_thread()
     print(json.dumps(line), flush=True)
     return 0
 

@@ -23,7 +23,8 @@ NORM_RMS_PER_HEAD, NORM_LAYER_ACROSS_HEADS = 0, 1
 EXPORTED = ("dit_attn_build_token_metadata", "dit_attn_build_key_valid", "dit_attn_qknorm_rope",
             "dit_attn_qknorm_rope_ex", "dit_attn_time_aware_rope_factors", "dit_attn_forward",
             "dit_attn_forward_cached", "dit_attn_forward_padded", "dit_attn_forward_cached_padded",
-            "dit_attn_forward_cached_qnorm", "dit_attn_cfg_norm_rescale", "dit_attn_status_string")
+            "dit_attn_forward_cached_qnorm", "dit_attn_cfg_norm_rescale", "dit_attn_prescaled_q_factor",
+            "dit_attn_status_string")
 
 
 class TokenMetaStruct(ctypes.Structure):
@@ -71,6 +72,7 @@ def _load() -> ctypes.CDLL:
                                                   i32, ctypes.POINTER(i32), ctypes.POINTER(NormRopeParams), f32, i32,
                                                   vp]
     lib.dit_attn_cfg_norm_rescale.argtypes = [vp, vp, vp, i64, i32, i64, i64, i64, f32, i32, vp]
+    lib.dit_attn_prescaled_q_factor.argtypes = [i32, f32, ctypes.POINTER(f32)]
     for name in EXPORTED[:-1]:
         getattr(lib, name).restype = ctypes.c_int
     lib.dit_attn_status_string.argtypes = [i32]

@@ -7,7 +7,6 @@ stream; outputs the caller does not pass are allocated with torch.
 from __future__ import annotations
 
 import ctypes
-import math
 from dataclasses import dataclass
 from typing import Optional, Sequence, Tuple, Union
 
@@ -20,7 +19,8 @@ __all__ = ["TokenMeta", "KeyValid", "DitAttnError", "LN2", "LOG2E", "prescaled_q
            "dit_attn_build_token_metadata", "dit_attn_build_key_valid", "dit_attn_qknorm_rope",
            "dit_attn_qknorm_rope_ex", "dit_attn_time_aware_rope_factors", "dit_attn_forward",
            "dit_attn_forward_cached", "dit_attn_forward_padded", "dit_attn_forward_cached_padded",
-           "dit_attn_forward_cached_qnorm", "dit_attn_cfg_norm_rescale", "build_token_metadata", "build_key_valid", "qknorm_rope",
+           "dit_attn_forward_cached_qnorm", "dit_attn_cfg_norm_rescale", "dit_attn_prescaled_q_factor",
+           "build_token_metadata", "build_key_valid", "qknorm_rope",
            "time_aware_rope_factors", "forward", "forward_cached", "forward_cached_qnorm", "cfg_norm_rescale"]
 
 _POS = {"centered_fhw": _lib.POS_CENTERED_FHW, "grid_hw": _lib.POS_GRID_HW}
@@ -32,9 +32,13 @@ LN2 = 0.6931471805599453
 def prescaled_q_factor(head_dim: int, softmax_scale: Optional[float] = None) -> float:
     """q_scale for dit_attn_qknorm_rope that folds the softmax scale (default
     1/sqrt(head_dim)) and log2(e) into Q; then call the attention with
-    softmax_scale=LN2."""
-    scale = softmax_scale if softmax_scale else 1.0 / math.sqrt(head_dim)
-    return scale * LOG2E
+    softmax_scale=LN2 (dit_attn_prescaled_q_factor)."""
+    out = ctypes.c_float()
+    check(lib.dit_attn_prescaled_q_factor(int(head_dim), float(softmax_scale or 0.0), ctypes.byref(out)),
+          "dit_attn_prescaled_q_factor")
+    return out.value
+
+
 _MASK = {"full": _lib.MASK_FULL, "block_causal": _lib.MASK_BLOCK_CAUSAL}
 
 
@@ -151,11 +155,29 @@ def dit_attn_build_key_valid(image_pad_mask: torch.Tensor, text_valid: torch.Ten
     return kv
 
 
-def _key_bits(key_valid) -> Tuple[int, int]:
+def _key_bits(key_valid, B: int, n_keys: int) -> Tuple[int, int]:
+    """Pointer and row stride of the key-validity words: one row per sample
+    and at least one word per 64 keys of the logical sequence."""
     bits = key_valid.bits if isinstance(key_valid, KeyValid) else key_valid
     if bits.dtype != torch.int64 or bits.dim() != 2 or bits.stride(1) != 1:
         raise DitAttnError(_lib.ERR_SHAPE, "key_valid bits must be int64 [B, words] with unit inner stride")
+    if bits.shape[0] != B or bits.shape[1] < (n_keys + 63) // 64:
+        raise DitAttnError(_lib.ERR_SHAPE, "key_valid bits must be [%d, >= %d] (one row per sample, one word per "
+                           "64 keys)" % (B, (n_keys + 63) // 64))
+    if bits.device.type != "cuda":
+        raise DitAttnError(_lib.ERR_UNSUPPORTED, "key_valid bits must be in device memory")
     return bits.data_ptr(), bits.stride(0) if bits.shape[0] > 1 else bits.shape[1]
+
+
+def _out_buffer(out: Optional[torch.Tensor], like: torch.Tensor, name: str) -> torch.Tensor:
+    """The caller's output buffer, checked to be exactly the shape and dtype of
+    `like` (the C ABI cannot see allocation sizes), or a new one."""
+    if out is None:
+        return torch.empty_like(like, memory_format=torch.contiguous_format)
+    if out.shape != like.shape or out.dtype != like.dtype or out.device != like.device:
+        raise DitAttnError(_lib.ERR_SHAPE, "%s must be %s %s on %s like the queries" % (
+            name, tuple(like.shape), like.dtype, like.device))
+    return out
 
 
 _NORM = {"rms_per_head": _lib.NORM_RMS_PER_HEAD, "layer_across_heads": _lib.NORM_LAYER_ACROSS_HEADS}
@@ -255,22 +277,33 @@ def dit_attn_qknorm_rope_ex(q, k, pos_ids, axes_dims, eps, norm="rms_per_head", 
     return q_out, k_out
 
 
-def _lse_buffer(return_lse: bool, B: int, H: int, S: int, device) -> Optional[torch.Tensor]:
+def _lse_buffer(return_lse: bool, lse_out: Optional[torch.Tensor], B: int, H: int, S: int,
+                device) -> Optional[torch.Tensor]:
+    """The lse output: the caller's fp32 [B, H, S] buffer (contiguous), a new
+    one when only return_lse is set, or None."""
+    if lse_out is not None:
+        if (lse_out.shape != (B, H, S) or lse_out.dtype != torch.float32 or not lse_out.is_contiguous()
+                or lse_out.device != torch.device(device)):
+            raise DitAttnError(_lib.ERR_SHAPE, "lse_out must be contiguous float32 [%d, %d, %d]" % (B, H, S))
+        return lse_out
     return torch.empty(B, H, S, dtype=torch.float32, device=device) if return_lse else None
 
 
 def dit_attn_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask_mode: Union[str, int] = "full",
                      meta: Optional[TokenMeta] = None, softmax_scale: Optional[float] = None,
                      out: Optional[torch.Tensor] = None, return_lse: bool = False, stream=None,
-                     key_valid=None):
+                     key_valid=None, lse_out: Optional[torch.Tensor] = None):
     """Attention over the joint sequence; with key_valid (a KeyValid or its
-    int64 bits [B, words]) padded keys are left out (dit_attn_forward_padded)."""
+    int64 bits [B, words]) padded keys are left out (dit_attn_forward_padded).
+    out / lse_out: caller buffers for O ([B, S, H, D]) and the lse (fp32
+    [B, H, S]); lse_out implies return_lse."""
     B, S, H, D = q.shape
     Hk = k.shape[2]
     if k.shape != (B, S, Hk, D) or v.shape != (B, S, Hk, D):
         raise DitAttnError(_lib.ERR_SHAPE, "k/v must be [B, S, H_kv, D] matching q")
-    o = out if out is not None else torch.empty_like(q, memory_format=torch.contiguous_format)
-    lse = _lse_buffer(return_lse, B, H, S, q.device)
+    o = _out_buffer(out, q, "out")
+    return_lse = return_lse or lse_out is not None
+    lse = _lse_buffer(return_lse, lse_out, B, H, S, q.device)
     strides = (_lib.Strides3 * 4)(_bshd_strides(q, "q"), _bshd_strides(k, "k"), _bshd_strides(v, "v"),
                                   _bshd_strides(o, "out"))
     dt = _dtype_code(q)
@@ -285,7 +318,7 @@ def dit_attn_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask_mod
                                   strides, mode, msp, scale, dt, _stream(stream))
         check(st, "dit_attn_forward")
     else:
-        kb, kbs = _key_bits(key_valid)
+        kb, kbs = _key_bits(key_valid, B, S)
         st = lib.dit_attn_forward_padded(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _ptr(lse), B, S, H,
                                          Hk, D, strides, mode, msp, kb, kbs, scale, dt, _stream(stream))
         check(st, "dit_attn_forward_padded")
@@ -296,10 +329,10 @@ def dit_attn_forward_cached(q_new: torch.Tensor, k_cache: Optional[torch.Tensor]
                             k_new: torch.Tensor, v_new: torch.Tensor, mask_mode: Union[str, int] = "block_causal",
                             meta: Optional[TokenMeta] = None, softmax_scale: Optional[float] = None,
                             out: Optional[torch.Tensor] = None, return_lse: bool = False, stream=None,
-                            key_valid=None):
+                            key_valid=None, lse_out: Optional[torch.Tensor] = None):
     """Attention of the new tokens against cache + new keys; with key_valid
     (bits over the logical sequence) padded keys are left out
-    (dit_attn_forward_cached_padded)."""
+    (dit_attn_forward_cached_padded).  out / lse_out as for forward."""
     B, S_new, H, D = q_new.shape
     Hk = k_new.shape[2]
     P = 0 if k_cache is None else k_cache.shape[1]
@@ -307,8 +340,9 @@ def dit_attn_forward_cached(q_new: torch.Tensor, k_cache: Optional[torch.Tensor]
         raise DitAttnError(_lib.ERR_SHAPE, "k_new/v_new must be [B, S_new, H_kv, D]")
     if P > 0 and (k_cache.shape != (B, P, Hk, D) or v_cache is None or v_cache.shape != (B, P, Hk, D)):
         raise DitAttnError(_lib.ERR_SHAPE, "k_cache/v_cache must be [B, P, H_kv, D]")
-    o = out if out is not None else torch.empty_like(q_new, memory_format=torch.contiguous_format)
-    lse = _lse_buffer(return_lse, B, H, S_new, q_new.device)
+    o = _out_buffer(out, q_new, "out")
+    return_lse = return_lse or lse_out is not None
+    lse = _lse_buffer(return_lse, lse_out, B, H, S_new, q_new.device)
     zero = _lib.Strides3(0, 0, 0)
     strides = (_lib.Strides3 * 6)(_bshd_strides(q_new, "q_new"),
                                   _bshd_strides(k_cache, "k_cache") if P > 0 else zero,
@@ -327,7 +361,7 @@ def dit_attn_forward_cached(q_new: torch.Tensor, k_cache: Optional[torch.Tensor]
                                          _stream(stream))
         check(st, "dit_attn_forward_cached")
     else:
-        kb, kbs = _key_bits(key_valid)
+        kb, kbs = _key_bits(key_valid, B, P + S_new)
         st = lib.dit_attn_forward_cached_padded(q_new.data_ptr(), kc, vc, k_new.data_ptr(), v_new.data_ptr(),
                                                 o.data_ptr(), _ptr(lse), B, P, S_new, H, Hk, D, strides, mode, msp,
                                                 kb, kbs, scale, dt, _stream(stream))
@@ -336,14 +370,16 @@ def dit_attn_forward_cached(q_new: torch.Tensor, k_cache: Optional[torch.Tensor]
 
 
 def dit_attn_forward_padded(q, k, v, key_valid, mask_mode="full", meta=None, softmax_scale=None, out=None,
-                            return_lse=False, stream=None):
-    return dit_attn_forward(q, k, v, mask_mode, meta, softmax_scale, out, return_lse, stream, key_valid=key_valid)
+                            return_lse=False, stream=None, lse_out=None):
+    return dit_attn_forward(q, k, v, mask_mode, meta, softmax_scale, out, return_lse, stream, key_valid=key_valid,
+                            lse_out=lse_out)
 
 
 def dit_attn_forward_cached_padded(q_new, k_cache, v_cache, k_new, v_new, key_valid, mask_mode="block_causal",
-                                   meta=None, softmax_scale=None, out=None, return_lse=False, stream=None):
+                                   meta=None, softmax_scale=None, out=None, return_lse=False, stream=None,
+                                   lse_out=None):
     return dit_attn_forward_cached(q_new, k_cache, v_cache, k_new, v_new, mask_mode, meta, softmax_scale, out,
-                                   return_lse, stream, key_valid=key_valid)
+                                   return_lse, stream, key_valid=key_valid, lse_out=lse_out)
 
 
 def dit_attn_forward_cached_qnorm(q_raw: torch.Tensor, k_cache: Optional[torch.Tensor],
@@ -354,7 +390,7 @@ def dit_attn_forward_cached_qnorm(q_raw: torch.Tensor, k_cache: Optional[torch.T
                                   q_scale: float = 1.0, mask_mode: Union[str, int] = "block_causal",
                                   meta: Optional[TokenMeta] = None, softmax_scale: Optional[float] = None,
                                   out: Optional[torch.Tensor] = None, return_lse: bool = False, stream=None,
-                                  key_valid=None):
+                                  key_valid=None, lse_out: Optional[torch.Tensor] = None):
     """Attention on raw Q: the kernel applies Q's per-head RMSNorm (weight
     q_weight), its rotary embedding (positions pos_ids [S_new, 3] of the query
     tokens, i.e. meta.pos_ids[P:]) and the softmax scale as it loads Q.  K
@@ -372,8 +408,9 @@ def dit_attn_forward_cached_qnorm(q_raw: torch.Tensor, k_cache: Optional[torch.T
     if q_weight is not None and (q_weight.dtype != q_raw.dtype or q_weight.numel() != D
                                  or not q_weight.is_contiguous()):
         raise DitAttnError(_lib.ERR_SHAPE, "q_weight must be contiguous [%d] in the input dtype" % D)
-    o = out if out is not None else torch.empty_like(q_raw, memory_format=torch.contiguous_format)
-    lse = _lse_buffer(return_lse, B, H, S_new, q_raw.device)
+    o = _out_buffer(out, q_raw, "out")
+    return_lse = return_lse or lse_out is not None
+    lse = _lse_buffer(return_lse, lse_out, B, H, S_new, q_raw.device)
     zero = _lib.Strides3(0, 0, 0)
     strides = (_lib.Strides3 * 6)(_bshd_strides(q_raw, "q_raw"),
                                   _bshd_strides(k_cache, "k_cache") if P > 0 else zero,
@@ -388,7 +425,7 @@ def dit_attn_forward_cached_qnorm(q_raw: torch.Tensor, k_cache: Optional[torch.T
     msp = ctypes.byref(ms) if ms is not None else None
     scale = 0.0 if softmax_scale is None else float(softmax_scale)
     kc, vc = (_ptr(k_cache), _ptr(v_cache)) if P > 0 else (None, None)
-    kb, kbs = _key_bits(key_valid) if key_valid is not None else (None, 0)
+    kb, kbs = _key_bits(key_valid, B, P + S_new) if key_valid is not None else (None, 0)
     axes = (ctypes.c_int32 * len(axes_dims))(*[int(a) for a in axes_dims])
     p = _lib.NormRopeParams(_lib.NORM_RMS_PER_HEAD, _ptr(q_weight), None, None, None, float(eps), float(rope_theta),
                             float(rope_linear_factor), float(rope_ntk_factor), float(q_scale))
@@ -430,6 +467,7 @@ def dit_attn_cfg_norm_rescale(cond: torch.Tensor, uncond: torch.Tensor, guidance
     return out
 
 
+dit_attn_prescaled_q_factor = prescaled_q_factor
 build_token_metadata = dit_attn_build_token_metadata
 cfg_norm_rescale = dit_attn_cfg_norm_rescale
 build_key_valid = dit_attn_build_key_valid

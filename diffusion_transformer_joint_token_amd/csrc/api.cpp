@@ -254,6 +254,14 @@ int dit_attn_time_aware_rope_factors(float t, float watershed, float scaling_fac
   return DIT_ATTN_OK;
 }
 
+int dit_attn_prescaled_q_factor(int32_t head_dim, float softmax_scale, float* q_scale_out) {
+  if (!q_scale_out) return DIT_ATTN_ERR_NULL;
+  if (head_dim < 1 || !std::isfinite(softmax_scale)) return DIT_ATTN_ERR_SHAPE;
+  const double scale = softmax_scale > 0.f ? (double)softmax_scale : 1.0 / std::sqrt((double)head_dim);
+  *q_scale_out = (float)(scale * 1.4426950408889634);
+  return DIT_ATTN_OK;
+}
+
 // Fused Q norm for attention_common (NULL: Q is already normed and rotated).
 struct QNormArgs {
   const void* q_weight;

@@ -231,6 +231,15 @@ int dit_attn_qknorm_rope_ex(const void *q, const void *k, void *q_out, void *k_o
 int dit_attn_time_aware_rope_factors(float t, float watershed, float scaling_factor,
                                      float *linear_factor, float *ntk_factor);
 
+/* Host helper: the q_scale that folds the attention's softmax scale into Q'
+ * (the scale of the pages' attention is 1/sqrt(head_dim) when none is given,
+ * as in scaled dot-product attention) together with log2(e), so that the
+ * attention can run with softmax_scale = ln 2 and exponentiate its logits in
+ * base 2: *q_scale_out = (softmax_scale > 0 ? softmax_scale : 1/sqrt(head_dim))
+ * * log2(e), evaluated in double and rounded once to float.  Errors: NULL
+ * output, head_dim < 1, a non-finite softmax_scale. */
+int dit_attn_prescaled_q_factor(int32_t head_dim, float softmax_scale, float *q_scale_out);
+
 /* Masked softmax attention (QwenImage21Transformer2DModel API page, block-causal
  * attention; NucleusMoE-Image article section 6.3 for GQA):
  *   O[b,q,h] = sum_k softmax_k(scale * <Q[b,q,h], K[b,k,g]>) V[b,k,g],  g = h / (H/H_kv)

@@ -19,6 +19,7 @@ from workloads import bf16_bits_to_f64, bf16_round_bits
 ATOL_BF16 = 1e-2
 MEAN_BF16 = 1e-3
 ATOL_F32 = 1e-5
+QUERY_TILE = 128  # query rows per work-group of the bf16 attention launch
 
 
 def to_device(bits: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
@@ -63,3 +64,72 @@ def assert_parity(gpu: np.ndarray, ora: np.ndarray, dtype: str, what: str, atol=
             what, err[worst], worst, gpu[worst], ora[worst])
         mean = float(np.mean(err))
     return {"max": float(err.max()), "mean": mean}
+
+
+def assert_literal_mean(gpu: np.ndarray, ora: np.ndarray, what: str) -> float:
+    """The stated mean-abs bar taken literally: mean |gpu - oracle| <= 1e-3
+    against the unrounded oracle.  Used at full size, where O is far below 1
+    in magnitude and the output format's own rounding is far below the bar."""
+    mean = float(np.mean(np.abs(np.asarray(gpu, np.float64) - np.asarray(ora, np.float64))))
+    assert mean <= MEAN_BF16, "%s: mean |gpu - oracle| %.3g > %.3g" % (what, mean, MEAN_BF16)
+    return mean
+
+
+def sample_rows(w, n_random=24, seed=0):
+    """Query rows (indices into the query tokens) for full-size checks: the
+    first and last rows, rows around every segment boundary, one row drawn in
+    every 128-row query tile -- so every work-group of the launch (one per
+    batch, head and query tile; the oracle computes all batches and heads of a
+    row) is compared -- and n_random more random rows."""
+    S = w.n_new
+    rows = {0, 1, 2, 3, S - 1, S - 2, S - 3}
+    start = 0
+    for seg in w.layout:
+        n = seg[1] if seg[0] == "T" else seg[1] * seg[2] * seg[3]
+        for r in (start - 1, start, start + 1, start + n - 1):
+            q = r - w.prefix_len
+            if 0 <= q < S:
+                rows.add(q)
+        start += n
+    rng = np.random.default_rng(seed)
+    for t0 in range(0, S, QUERY_TILE):
+        rows.add(int(rng.integers(t0, min(S, t0 + QUERY_TILE))))
+    rows.update(int(x) for x in rng.integers(0, S, size=n_random))
+    out = np.array(sorted(rows))
+    assert set(out // QUERY_TILE) == set(range((S + QUERY_TILE - 1) // QUERY_TILE))
+    return out
+
+
+def nan_outputs(q: torch.Tensor):
+    """O and lse buffers for a call on queries q ([B, S, H, D]) filled with NaN,
+    so that any element the launch fails to write shows up."""
+    B, S, H, _ = q.shape
+    o = torch.full(q.shape, float("nan"), dtype=q.dtype, device=q.device)
+    lse = torch.full((B, H, S), float("nan"), dtype=torch.float32, device=q.device)
+    return o, lse
+
+
+def assert_all_written(o: torch.Tensor, lse: torch.Tensor, what: str, lse_may_be_neg_inf: bool = False):
+    """Every element of a NaN-prefilled O and lse was written with a finite
+    value (lse may be -inf on rows with no valid key, when padding allows it)."""
+    bad_o = int((~torch.isfinite(o)).sum())
+    assert bad_o == 0, "%s: %d elements of O not written or not finite" % (what, bad_o)
+    ok = torch.isfinite(lse)
+    if lse_may_be_neg_inf:
+        ok = ok | torch.isneginf(lse)
+    bad_l = int((~ok).sum())
+    assert bad_l == 0, "%s: %d lse entries not written or not finite" % (what, bad_l)
+
+
+def oracle_rows(attention, qp_rows, k_all, v_all, image_ids, mask_mode, P, rows, key_valid=None):
+    """The oracle's O and lse for the given query rows, computed one row at a
+    time (row r of the query tokens is logical position P + r)."""
+    B, _, H, D = np.asarray(qp_rows).shape
+    ro = np.zeros((B, rows.size, H, D))
+    rl = np.zeros((B, H, rows.size))
+    for j, r in enumerate(rows):
+        oj, lj = attention(qp_rows[:, j:j + 1], k_all, v_all, image_ids, mask_mode, q_offset=P + int(r),
+                           key_valid=key_valid)
+        ro[:, j] = oj[:, 0]
+        rl[:, :, j] = lj[:, :, 0]
+    return ro, rl

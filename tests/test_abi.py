@@ -298,3 +298,57 @@ def test_cfg_argument_errors():
     assert call(u=FAKE2 + 8) == _lib.ERR_ALIGN
     assert call(cs=68) == _lib.ERR_ALIGN               # 136-byte row stride
     assert call(rows=0, c=None) == _lib.OK
+
+
+def test_binding_checks_output_buffers_and_key_bits():
+    """The binding compares caller buffers with the call before it reaches the
+    C ABI (which cannot see allocation sizes): O must have the queries' shape
+    and dtype, lse_out must be fp32 [B, H, S], and the key-validity words must
+    have one row per sample and a word per 64 keys.  (CPU tensors: every case
+    raises before anything is launched.)"""
+    import torch
+    import diffusion_transformer_joint_token_amd as dit
+    bf = torch.bfloat16
+    q = torch.zeros(2, 70, 8, 128, dtype=bf)
+    k = v = torch.zeros(2, 70, 2, 128, dtype=bf)
+    bad_outs = [torch.zeros(2, 70, 2, 128, dtype=bf),      # GQA-shaped: the kernel would write past its end
+                torch.zeros(2, 70, 8, 128, dtype=torch.float32),
+                torch.zeros(1, 70, 8, 128, dtype=bf)]
+    for out in bad_outs:
+        with pytest.raises(dit.DitAttnError):
+            dit.forward(q, k, v, "full", out=out)
+        with pytest.raises(dit.DitAttnError):
+            dit.forward_cached(q, None, None, k, v, "full", out=out)
+        with pytest.raises(dit.DitAttnError):
+            dit.forward_cached_qnorm(q, None, None, k, v, torch.zeros(70, 3, dtype=torch.int32), (32, 48, 48),
+                                     1e-6, mask_mode="full", out=out)
+    for lse in (torch.zeros(2, 2, 70), torch.zeros(2, 8, 70, dtype=bf), torch.zeros(2, 70, 8)):
+        with pytest.raises(dit.DitAttnError):
+            dit.forward(q, k, v, "full", lse_out=lse)
+    for bits in (torch.zeros(1, 2, dtype=torch.int64),     # one row for two samples
+                 torch.zeros(2, 1, dtype=torch.int64),     # 70 keys need 2 words
+                 torch.zeros(2, 2, dtype=torch.int32)):
+        with pytest.raises(dit.DitAttnError):
+            dit.forward(q, k, v, "full", key_valid=bits)
+        with pytest.raises(dit.DitAttnError):
+            dit.forward_cached(q, None, None, k, v, "full", key_valid=bits)
+    # cached: the words cover the logical sequence P + S_new
+    kc = vc = torch.zeros(2, 64, 2, 128, dtype=bf)
+    with pytest.raises(dit.DitAttnError):
+        dit.forward_cached(q, kc, vc, k, v, "full", key_valid=torch.zeros(2, 2, dtype=torch.int64))
+
+
+def test_prescaled_factor_helper():
+    """dit_attn_prescaled_q_factor: (scale or 1/sqrt(D)) * log2(e), in double,
+    rounded once; the binding's prescaled_q_factor is that call."""
+    import math
+    from diffusion_transformer_joint_token_amd import _lib, api
+    out = ctypes.c_float()
+    for D, s in ((128, 0.0), (72, 0.0), (32, 0.0), (128, 0.3)):
+        assert _lib.lib.dit_attn_prescaled_q_factor(D, s, ctypes.byref(out)) == _lib.OK
+        want = ctypes.c_float((s if s > 0 else 1.0 / math.sqrt(D)) * 1.4426950408889634).value
+        assert out.value == want
+        assert api.prescaled_q_factor(D, s or None) == want
+    assert _lib.lib.dit_attn_prescaled_q_factor(128, 0.0, None) == _lib.ERR_NULL
+    assert _lib.lib.dit_attn_prescaled_q_factor(0, 0.0, ctypes.byref(out)) == _lib.ERR_SHAPE
+    assert _lib.lib.dit_attn_prescaled_q_factor(128, float("nan"), ctypes.byref(out)) == _lib.ERR_SHAPE

@@ -147,3 +147,12 @@ def test_clock_ramp_runs_whole_batches_until_the_time_is_up():
     assert _Cuda.syncs == n // 10
     _Cuda.syncs = 0
     assert bench.ramp_clocks(_Torch, lambda: None, 0.0) == 0 and _Cuda.syncs == 0
+
+
+def test_clock_reading_never_raises():
+    """The bench's clock record is a dict of MHz lists, or an error entry where
+    no device (or no amdsmi) is there, as on a CPU-only host; it never raises."""
+    import bench
+    got = bench.read_clocks()
+    assert isinstance(got, dict)
+    assert "error" in got or ("sclk_mhz" in got and "mclk_mhz" in got)

@@ -20,8 +20,8 @@ import oracle.key_padding as okp
 import oracle.metadata as ometa
 import oracle.qknorm_rope as oqr
 import workloads as wl
-from tests.gpu_helpers import assert_parity, rne_bf16, to_device, to_host
-from tests.test_gpu_parity import sample_rows
+from tests.gpu_helpers import (assert_all_written, assert_literal_mean, assert_parity, nan_outputs, oracle_rows,
+                               rne_bf16, sample_rows, to_device, to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -46,7 +46,8 @@ def _check_lse(gpu_lse: np.ndarray, ref: np.ndarray, what="lse"):
 
 
 def _fused(dit, w, d, m, kv=None, unit=False):
-    """K-only norm, then attention on raw Q; returns (o, lse, k')."""
+    """K-only norm, then attention on raw Q into NaN-filled O and lse
+    buffers; returns (o, lse, k')."""
     P = w.prefix_len
     q, k, v = (to_device(d.bits[n], w.dtype) for n in ("q", "k", "v"))
     wq = None if unit else to_device(d.bits["wq"], w.dtype)
@@ -56,8 +57,9 @@ def _fused(dit, w, d, m, kv=None, unit=False):
     assert qo is None
     kc = to_device(d.bits["k_cache"], w.dtype) if P else None
     vc = to_device(d.bits["v_cache"], w.dtype) if P else None
-    o, lse = dit.forward_cached_qnorm(q, kc, vc, kp, v, m.pos_ids[P:], w.axes, w.eps, q_weight=wq,
-                                      mask_mode=w.mask_mode, meta=m, return_lse=True, key_valid=kv, **rk)
+    o, lse = nan_outputs(q)
+    dit.forward_cached_qnorm(q, kc, vc, kp, v, m.pos_ids[P:], w.axes, w.eps, q_weight=wq, mask_mode=w.mask_mode,
+                             meta=m, key_valid=kv, out=o, lse_out=lse, **rk)
     torch.cuda.synchronize()
     return o, lse, kp
 
@@ -104,7 +106,8 @@ def test_fused_qnorm_attention_all_rows(dit, case):
     it.  The reference O and lse take the oracle's Q' and K' through those
     same two roundings.  (Rows with one to three valid keys, which random
     text padding makes, move by up to ~1e-2 under these roundings alone, as
-    they do in the two-kernel path.)"""
+    they do in the two-kernel path.)  Without padding every output is also
+    held to the bar against the unrounded oracle's Q' and K'."""
     B, H, Hk, D, layout, axes, mode, P, unit, kind = case[:10]
     lin, ntk = case[10:12] if len(case) > 10 else (1.0, 1.0)
     w = wl.small_workload("f", B, H, Hk, D, layout, axes, mask_mode=mode, seed=5 * D + P, prefix_len=P,
@@ -132,8 +135,14 @@ def test_fused_qnorm_attention_all_rows(dit, case):
     k_all = np.concatenate([d.vals["k_cache"], rk_in], axis=1) if P else rk_in
     v_all = np.concatenate([d.vals["v_cache"], d.vals["v"]], axis=1) if P else d.vals["v"]
     ro, rl = oatt.attention(rq_in, k_all, v_all, md["image_ids"], mode, q_offset=P, key_valid=valid)
+    assert_all_written(o, lse, "fused", lse_may_be_neg_inf=kind is not None)
     assert_parity(to_host(o), ro, "bf16", "O")
     _check_lse(lse.cpu().double().numpy(), rl)
+    if kind is None:
+        k_all = np.concatenate([d.vals["k_cache"], rk], axis=1) if P else rk
+        ro_u, rl_u = oatt.attention(rq, k_all, v_all, md["image_ids"], mode, q_offset=P)
+        assert_parity(to_host(o), ro_u, "bf16", "O (unrounded Q', K')")
+        _check_lse(lse.cpu().double().numpy(), rl_u, "lse (unrounded Q', K')")
 
 
 def test_fused_matches_two_kernel_path(dit):
@@ -211,7 +220,8 @@ FULL = [n for n in list(wl.WORKLOADS) + list(wl.VARIANTS)
 @pytest.mark.parametrize("name", FULL)
 def test_fused_workloads_sampled(dit, name):
     """The fused step at full size, in the launch configuration the benchmark
-    times; the oracle computes sampled query rows one by one."""
+    times: every element of O and lse written, and sampled query rows (at
+    least one in every 128-row query tile) against the unrounded oracle."""
     w = wl.get(name)
     _say("fused workload %s" % name)
     d = wl.draw(w)
@@ -220,6 +230,7 @@ def test_fused_workloads_sampled(dit, name):
     m = dit.build_token_metadata(torch.from_numpy(mask).cuda(), shapes, w.pos_mode)
     m.check()
     o, lse, _ = _fused(dit, w, d, m)
+    assert_all_written(o, lse, name)
     P = w.prefix_len
     rows = sample_rows(w)
     pos = md["pos_ids"][P:]
@@ -227,16 +238,12 @@ def test_fused_workloads_sampled(dit, name):
     kp = oqr.qknorm_rope(d.vals["k"], d.vals["wk"], w.eps, pos, w.axes)
     k_all = np.concatenate([d.vals["k_cache"], kp], axis=1) if P else kp
     v_all = np.concatenate([d.vals["v_cache"], d.vals["v"]], axis=1) if P else d.vals["v"]
-    ro = np.zeros((w.batch, rows.size, w.heads, w.head_dim))
-    rl = np.zeros((w.batch, w.heads, rows.size))
-    for j, r in enumerate(rows):
-        oj, lj = oatt.attention(qp[:, j:j + 1], k_all, v_all, md["image_ids"], w.mask_mode, q_offset=P + int(r))
-        ro[:, j] = oj[:, 0]
-        rl[:, :, j] = lj[:, :, 0]
+    ro, rl = oracle_rows(oatt.attention, qp, k_all, v_all, md["image_ids"], w.mask_mode, P, rows)
     idx = torch.from_numpy(rows).cuda()
     stats = assert_parity(to_host(o[:, idx]), ro, "bf16", "O")
+    lit = assert_literal_mean(to_host(o[:, idx]), ro, "O")
     assert_parity(lse[:, :, idx].cpu().double().numpy(), rl, "f32", "lse", atol=1e-2)
-    _say("  %s rows=%d max=%.3g mean=%.3g" % (name, rows.size, stats["max"], stats["mean"]))
+    _say("  %s rows=%d max=%.3g mean=%.3g (unrounded %.3g)" % (name, rows.size, stats["max"], stats["mean"], lit))
 
 
 def test_fused_padded_workload_sampled(dit):
@@ -251,19 +258,16 @@ def test_fused_padded_workload_sampled(dit):
     kv = dit.build_key_valid(torch.from_numpy(mask).cuda(), torch.from_numpy(tv).cuda())
     kv.check()
     o, lse, _ = _fused(dit, w, d, m, kv)
+    assert_all_written(o, lse, "padded headline", lse_may_be_neg_inf=True)
     rows = sample_rows(w, seed=3)
     pos = md["pos_ids"]
     qp = oqr.qknorm_rope(d.vals["q"][:, rows], d.vals["wq"], w.eps, pos[rows], w.axes)
     kp = oqr.qknorm_rope(d.vals["k"], d.vals["wk"], w.eps, pos, w.axes)
-    ro = np.zeros((w.batch, rows.size, w.heads, w.head_dim))
-    rl = np.zeros((w.batch, w.heads, rows.size))
-    for j, r in enumerate(rows):
-        oj, lj = oatt.attention(qp[:, j:j + 1], kp, d.vals["v"], md["image_ids"], w.mask_mode, q_offset=int(r),
-                                key_valid=valid)
-        ro[:, j] = oj[:, 0]
-        rl[:, :, j] = lj[:, :, 0]
+    ro, rl = oracle_rows(oatt.attention, qp, kp, d.vals["v"], md["image_ids"], w.mask_mode, 0, rows,
+                         key_valid=valid)
     idx = torch.from_numpy(rows).cuda()
     assert_parity(to_host(o[:, idx]), ro, "bf16", "O")
+    assert_literal_mean(to_host(o[:, idx]), ro, "O")
     _check_lse(lse[:, :, idx].cpu().double().numpy(), rl)
 
 

@@ -16,8 +16,8 @@ import oracle.attention as oatt
 import oracle.metadata as ometa
 import oracle.qknorm_rope as oqr
 import workloads as wl
-from tests.gpu_helpers import assert_parity, to_device, to_host
-from tests.test_gpu_parity import sample_rows
+from tests.gpu_helpers import (assert_all_written, assert_literal_mean, assert_parity, nan_outputs, sample_rows,
+                               to_device, to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -135,8 +135,10 @@ def test_lumina_2k_variant_pipeline(dit):
     kw = dict(norm=w.qk_norm, q_bias=bq, k_bias=bk, rope_linear_factor=w.rope_linear, rope_ntk_factor=w.rope_ntk)
     qp0, kp = dit.qknorm_rope(q, k, m.pos_ids, w.axes, w.eps, wq, wk, **kw)
     qp, _ = dit.qknorm_rope(q, k, m.pos_ids, w.axes, w.eps, wq, wk, q_scale=dit.prescaled_q_factor(w.head_dim), **kw)
-    o, lse = dit.forward(qp, kp, v, w.mask_mode, m, softmax_scale=dit.LN2, return_lse=True)
+    o, lse = nan_outputs(q)
+    dit.forward(qp, kp, v, w.mask_mode, m, softmax_scale=dit.LN2, out=o, lse_out=lse)
     torch.cuda.synchronize()
+    assert_all_written(o, lse, w.name)
     okw = dict(norm=w.qk_norm, linear_factor=w.rope_linear, ntk_factor=w.rope_ntk)
     rows = sample_rows(w, 40)
     idx = torch.from_numpy(rows).cuda()
@@ -147,5 +149,6 @@ def test_lumina_2k_variant_pipeline(dit):
     assert_parity(to_host(kp[:, idx]), rk[:, rows], w.dtype, "k'")
     ro, rl = oatt.attention(rq, rk, d.vals["v"], md["image_ids"], w.mask_mode)
     stats = assert_parity(to_host(o[:, idx]), ro, w.dtype, "O")
+    assert_literal_mean(to_host(o[:, idx]), ro, "O")
     assert_parity(lse[:, :, idx].cpu().double().numpy(), rl, "f32", "lse", atol=1e-2)
     _say("  rows=%d max=%.3g mean=%.3g" % (rows.size, stats["max"], stats["mean"]))

@@ -20,8 +20,8 @@ import oracle.key_padding as okp
 import oracle.metadata as ometa
 import oracle.qknorm_rope as oqr
 import workloads as wl
-from tests.gpu_helpers import assert_parity, to_device, to_host
-from tests.test_gpu_parity import sample_rows
+from tests.gpu_helpers import (assert_all_written, assert_literal_mean, assert_parity, nan_outputs, oracle_rows,
+                               sample_rows, to_device, to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -310,28 +310,26 @@ def test_padded_pipeline_workloads(dit, name):
     wq, wk = to_device(d.bits["wq"], w.dtype), to_device(d.bits["wk"], w.dtype)
     qp, kp = dit.qknorm_rope(q, k, m.pos_ids[P:], w.axes, w.eps, wq, wk,
                              q_scale=dit.prescaled_q_factor(w.head_dim))
+    o, lse = nan_outputs(q)
     if P:
         kc, vc = to_device(d.bits["k_cache"], w.dtype), to_device(d.bits["v_cache"], w.dtype)
-        o, lse = dit.forward_cached(qp, kc, vc, kp, v, w.mask_mode, m, softmax_scale=dit.LN2, return_lse=True,
-                                    key_valid=kv)
+        dit.forward_cached(qp, kc, vc, kp, v, w.mask_mode, m, softmax_scale=dit.LN2, key_valid=kv, out=o,
+                           lse_out=lse)
     else:
-        o, lse = dit.forward(qp, kp, v, w.mask_mode, m, softmax_scale=dit.LN2, return_lse=True, key_valid=kv)
+        dit.forward(qp, kp, v, w.mask_mode, m, softmax_scale=dit.LN2, key_valid=kv, out=o, lse_out=lse)
     torch.cuda.synchronize()
+    # a right-padded prefix of at least one valid text token leaves every row a key
+    assert_all_written(o, lse, name)
     rows = sample_rows(w)
     pos = md["pos_ids"][P:]
     rq = oqr.qknorm_rope(d.vals["q"][:, rows], d.vals["wq"], w.eps, pos[rows], w.axes)
     rk = oqr.qknorm_rope(d.vals["k"], d.vals["wk"], w.eps, pos, w.axes)
     k_all = np.concatenate([d.vals["k_cache"], rk], axis=1) if P else rk
     v_all = np.concatenate([d.vals["v_cache"], d.vals["v"]], axis=1) if P else d.vals["v"]
-    ro = np.zeros((w.batch, rows.size, w.heads, w.head_dim))
-    rl = np.zeros((w.batch, w.heads, rows.size))
-    for j, r in enumerate(rows):
-        oj, lj = oatt.attention(rq[:, j:j + 1], k_all, v_all, md["image_ids"], w.mask_mode, q_offset=P + int(r),
-                                key_valid=valid)
-        ro[:, j] = oj[:, 0]
-        rl[:, :, j] = lj[:, :, 0]
+    ro, rl = oracle_rows(oatt.attention, rq, k_all, v_all, md["image_ids"], w.mask_mode, P, rows, key_valid=valid)
     idx = torch.from_numpy(rows).cuda()
     stats = assert_parity(to_host(o[:, idx]), ro, w.dtype, "O")
+    assert_literal_mean(to_host(o[:, idx]), ro, "O")
     _check_lse(lse[:, :, idx].cpu().double().numpy(), rl, w.dtype)
     _say("  %s valid text %s rows=%d max=%.3g mean=%.3g" % (name, tv.sum(axis=1).tolist(), rows.size,
                                                             stats["max"], stats["mean"]))
@@ -390,9 +388,10 @@ def test_image_query_workload_sampled(dit):
     kc, vc = to_device(d.bits["k_cache"], w.dtype), to_device(d.bits["v_cache"], w.dtype)
     qp, kp = dit.qknorm_rope(q, k, m.pos_ids[P:], w.axes, w.eps, wq, wk,
                              q_scale=dit.prescaled_q_factor(w.head_dim))
-    o, lse = dit.forward_cached(qp, kc, vc, kp, v, "full", m, softmax_scale=dit.LN2, return_lse=True,
-                                key_valid=kv)
+    o, lse = nan_outputs(q)
+    dit.forward_cached(qp, kc, vc, kp, v, "full", m, softmax_scale=dit.LN2, key_valid=kv, out=o, lse_out=lse)
     torch.cuda.synchronize()
+    assert_all_written(o, lse, w.name)
     rows = sample_rows(w)
     pos = md["pos_ids"][P:]
     rq = oqr.qknorm_rope(d.vals["q"][:, rows], d.vals["wq"], w.eps, pos[rows], w.axes)
@@ -402,6 +401,7 @@ def test_image_query_workload_sampled(dit):
     ro, rl = oatt.attention(rq, k_all, v_all, md["image_ids"], "full", q_offset=P, key_valid=valid)
     idx = torch.from_numpy(rows).cuda()
     stats = assert_parity(to_host(o[:, idx]), ro, w.dtype, "O")
+    assert_literal_mean(to_host(o[:, idx]), ro, "O")
     _check_lse(lse[:, :, idx].cpu().double().numpy(), rl, w.dtype)
     _say("  valid text %s rows=%d max=%.3g mean=%.3g" % (tv.sum(axis=1).tolist(), rows.size, stats["max"],
                                                         stats["mean"]))
