@@ -359,7 +359,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   auto issue = [&](int t, char* dst, bool is_k) __attribute__((always_inline)) {
     const bool live = t < n_tiles;
     const int k0 = live ? t * kTileN : 0;
-    char* d0 = dst + 1024 * wv;
+    // The wave's LDS offset goes through an opaque copy at every issue, so
+    // the load destinations (M0 values) are formed where they are used
+    // instead of being hoisted, sixteen of them, into scalar registers that
+    // stay live across the loop.
+    int wofs = 1024 * wv;
+    asm volatile("" : "+s"(wofs));
+    char* d0 = dst + wofs;
     if (ALIGNED || k0 + kTileN <= P || k0 >= P) {
       const bool cached = k0 < P;
       const __amdgpu_buffer_rsrc_t r =
@@ -758,8 +764,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   const float l_tot = sum_with_partner32(l_own);
   const bool empty = PADDED && !(l_tot > 0.f);  // no valid key: O = 0, lse = -inf
   const float inv = empty ? 0.f : 1.0f / l_tot;
+  // The output arguments are read here, through an opaque copy of the
+  // kernel-argument pointer, so that they are not loaded at entry and held in
+  // scalar registers (or spilled) across the tile loop.
+  using const_args = const __attribute__((address_space(4))) AttnArgs;
+  const_args* ka = (const_args*)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(ka));
   if (row_ok) {
-    __bf16* op = reinterpret_cast<__bf16*>(a.o) + b * a.os[0] + (int64_t)qrow * a.os[1] + h * a.os[2];
+    __bf16* op = reinterpret_cast<__bf16*>(ka->o) + b * ka->os[0] + (int64_t)qrow * ka->os[1] + h * ka->os[2];
 #pragma unroll
     for (int mb = 0; mb < MBLK; ++mb) {
 #pragma unroll
@@ -773,9 +785,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
         }
       }
     }
-    if (a.lse != nullptr && g == 0)
-      a.lse[((int64_t)b * a.H + h) * a.Snew + qrow] =
-          empty ? -INFINITY : (m_off + __log2f(l_tot)) * 0.6931471805599453f;
+    float* lse = ka->lse;
+    if (lse != nullptr && g == 0)
+      lse[((int64_t)b * ka->H + h) * ka->Snew + qrow] = empty ? -INFINITY : (m_off + __log2f(l_tot)) * 0.6931471805599453f;
   }
 }
 
