@@ -420,7 +420,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   f32x16 oacc[MBLK];
 #pragma unroll
   for (int mb = 0; mb < MBLK; ++mb) oacc[mb] = f32x16{};
-  const float c2 = a.scale * 1.4426950408889634f;  // scale * log2(e); 1 when UNIT
+  const float c2 = UNIT ? 1.0f : a.scale * 1.4426950408889634f;  // scale * log2(e)
   const float ic2 = UNIT ? 1.0f : 1.0f / c2;
   float m_off = 0.f;   // running offset (log2 units)
   // Every S tile's accumulator starts here: -m_off in logit units, rebuilt only
@@ -468,8 +468,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   // mx: max of the tile's shifted logits (logit units).  Rows that grew past
   // the threshold (or see their first tile) move the offset to the tile max,
   // rescale O and l, and shift the tile's logits to the new offset.
+  // Without padding every row's first tile holds key 0, which it may see: the
+  // prologue moves the offset for S(0) (update_first) and the loop's test is
+  // the threshold alone.
   auto update = [&](float mx, f32x16 (&sacc)[2]) __attribute__((always_inline)) {
-    const bool grow = mx > -INFINITY && (fresh || mx * c2 > kLazyRescale);
+    const bool grow = PADDED ? mx > -INFINITY && (fresh || mx * c2 > kLazyRescale) : mx * c2 > kLazyRescale;
     if (__any(grow)) {
       const float d = grow ? mx : 0.f;
       const float alpha = fresh ? 0.f : __builtin_amdgcn_exp2f(-d * c2);
@@ -483,11 +486,15 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) s_init[i] = ni;
     }
-    // Without padding every row's first tile holds key 0, which it may see.
-    if constexpr (PADDED)
-      fresh = fresh && !(mx > -INFINITY);
-    else
-      fresh = false;
+    if constexpr (PADDED) fresh = fresh && !(mx > -INFINITY);
+  };
+  auto update_first = [&](float mx, f32x16 (&sacc)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) sacc[kb] -= mx;
+    m_off = mx * c2;
+    const float ni = -m_off * ic2;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s_init[i] = ni;
   };
   // P = exp2(c2 * S) as bf16 B operands; row sums from the same bf16 values.
   auto softmax = [&](const f32x16 (&sacc)[2], bf16x8 (&pop)[2][2]) __attribute__((always_inline)) {
@@ -656,7 +663,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
     asm volatile("" ::: "memory");
     qk(sK0, sA);
     if (kTileN > wlim_min) mask(0, sA, ~0ull);
-    mx_cur = rowmax(sA);
+    update_first(rowmax(sA), sA);
+    fresh = false;
+    mx_cur = -INFINITY;  // S(0) is shifted already: nothing to move in phase 1
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
     __builtin_amdgcn_s_barrier();  // every wave is done with K(0)
     asm volatile("" ::: "memory");
