@@ -136,6 +136,14 @@ def source_sha(path: str) -> str:
         return hashlib.sha256(fh.read()).hexdigest()
 
 
+def kernel_label(head_dim: int, padded: bool, fused: bool) -> str:
+    """Template instance of the bf16 attention kernel that a head dim runs:
+    the head dim rounded up to 32 channels, except 65..80 (Lumina-Next's 72),
+    which takes five 16-channel QK^T steps as an 80-channel instance."""
+    dp = 80 if 64 < head_dim <= 80 else (head_dim + 31) // 32 * 32
+    return "attn_fwd_bf16_kernel<%d,4%s%s>" % (dp, ",padded" if padded else "", ",qnorm" if fused else "")
+
+
 def measured_traffic(w, path: str = TRAFFIC_FILE, source: str = ATTN_SOURCE):
     """HBM bytes per launch from the committed rocprofv3 counter runs, or None
     when they were taken on another kernel source or workload."""
@@ -405,8 +413,7 @@ def measure_config(name: str, steps: int, warmup: int, ramp_s: float) -> dict:
            "attention_tflops": attn, "attention_frac_bf16_peak": attn / PEAK_BF16_TFLOPS,
            "qknorm_rope_ms": t["norm_ms"], "qknorm_rope_frac_hbm": norm_bytes / (t["norm_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
            "token_metadata_ms": t["meta_ms"],
-           "kernel": "attn_fwd_bf16_kernel<%d,4%s>" % (80 if 64 < w.head_dim <= 80 else (w.head_dim + 31) // 32 * 32,
-                                                       ",qnorm" if step.fused else "")}
+           "kernel": kernel_label(w.head_dim, False, step.fused)}
     del step
     torch.cuda.empty_cache()
     return out
@@ -759,9 +766,7 @@ def main(argv=None) -> int:
 
     roofline = {"bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": attn_tflops / PEAK_BF16_TFLOPS, "traffic": measured_traffic(w),
-                "kernel": "attn_fwd_bf16_kernel<%d,4%s%s>" % ((w.head_dim + 31) // 32 * 32,
-                                                              ",padded" if step.kv is not None else "",
-                                                              ",qnorm" if step.fused else ""),
+                "kernel": kernel_label(w.head_dim, step.kv is not None, step.fused),
                 "launch_ms_mean": t["attn_ms_mean"],
                 "launch_ms_min": t["attn_ms_min"], "flops_per_launch": flops}
     line = {

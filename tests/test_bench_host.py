@@ -156,3 +156,16 @@ def test_clock_reading_never_raises():
     got = bench.read_clocks()
     assert isinstance(got, dict)
     assert "error" in got or ("sclk_mhz" in got and "mclk_mhz" in got)
+
+
+@pytest.mark.parametrize("head_dim,padded,fused,want", [
+    (128, False, True, "attn_fwd_bf16_kernel<128,4,qnorm>"),
+    (72, False, True, "attn_fwd_bf16_kernel<80,4,qnorm>"),
+    (72, True, False, "attn_fwd_bf16_kernel<80,4,padded>"),
+    (96, False, False, "attn_fwd_bf16_kernel<96,4>"),
+    (40, False, False, "attn_fwd_bf16_kernel<64,4>"),
+])
+def test_kernel_label_names_the_launched_instance(head_dim, padded, fused, want):
+    """The label in the line names the template instance the launcher picks
+    for the head dim (65..80 runs as the 80-channel instance)."""
+    assert bench.kernel_label(head_dim, padded, fused) == want
