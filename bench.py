@@ -419,6 +419,33 @@ def measure_config(name: str, steps: int, warmup: int, ramp_s: float) -> dict:
     return out
 
 
+def library_gemm_reference(torch, n: int = 8192, seconds: float = 1.5) -> dict:
+    """The vendor library's bf16 GEMM (torch.matmul, hipBLASLt) on n x n x n
+    contiguous operands, timed back to back on the same card after a clock
+    ramp: the MFMA rate that dense library code reaches under the card's power
+    limit, beside the published peak (context for the roofline fraction)."""
+    x = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    y = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    z = torch.empty(n, n, device="cuda", dtype=torch.bfloat16)
+    run = lambda: torch.matmul(x, y, out=z)  # noqa: E731
+    ramp_clocks(torch, run, 0.4)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 50
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    clocks = clocks_under_load(torch, run, seconds)
+    tflops = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    del x, y, z
+    torch.cuda.empty_cache()
+    return {"op": "torch.matmul bf16 %dx%dx%d (hipBLASLt)" % (n, n, n), "ms": ms, "tflops": tflops,
+            "frac_bf16_peak": tflops / PEAK_BF16_TFLOPS, "clocks_under_load": clocks}
+
+
 def cpu_single_thread() -> dict:
     """The oracle on one host thread for the tiny fp32 workload (every query
     row) and the Lumina mini shape of the Lumina-Next article's standalone
@@ -684,6 +711,8 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-other-configs", action="store_true",
                     help="skip the step and attention timings of the other bf16 workloads (the line's `configs`)")
+    ap.add_argument("--no-gemm-reference", action="store_true",
+                    help="skip the library bf16 GEMM timed beside the attention (the line's `library_gemm`)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (the reference "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -812,6 +841,11 @@ def main(argv=None) -> int:
             log("config %s: %s" % (name, json.dumps(c)))
             line["configs"][name] = c
     line["clocks"] = {"before": clocks_before, "under_load": clocks_load, "after": read_clocks()}
+    if other and not args.no_gemm_reference:
+        g = library_gemm_reference(torch)
+        g["attention_vs_gemm"] = attn_tflops / g["tflops"]
+        log("library gemm: %s" % json.dumps(g))
+        line["library_gemm"] = g
     line["host"] = {"cpu_model": cpu_model(), "cores": len(os.sched_getaffinity(0))}
     if args.multistep:
         ms = multistep(step, args.multistep, args.steps, args.warmup, t["step_ms"], args.clock_ramp_s)
