@@ -144,6 +144,16 @@ def kernel_label(head_dim: int, padded: bool, fused: bool) -> str:
     return "attn_fwd_bf16_kernel<%d,4%s%s>" % (dp, ",padded" if padded else "", ",qnorm" if fused else "")
 
 
+def padded_work_factor(head_dim: int) -> float:
+    """MFMA work the bf16 kernel issues per useful FLOP from head-dim padding:
+    QK^T contracts over the instance's channel count (80 for 65..80, else the
+    head dim rounded up to 32) and PV produces 32-channel blocks, so
+    (qk + pv) / (2 * head_dim).  1.0 for head dims that are multiples of 32."""
+    qk = 80 if 64 < head_dim <= 80 else (head_dim + 31) // 32 * 32
+    pv = (head_dim + 31) // 32 * 32
+    return (qk + pv) / (2.0 * head_dim)
+
+
 def measured_traffic(w, path: str = TRAFFIC_FILE, source: str = ATTN_SOURCE):
     """HBM bytes per launch from the committed rocprofv3 counter runs, or None
     when they were taken on another kernel source or workload."""
@@ -411,6 +421,7 @@ def measure_config(name: str, steps: int, warmup: int, ramp_s: float) -> dict:
            "step_ms": t["step_ms"], "step_tflops": flops / (t["step_ms"] * 1e-3) / 1e12,
            "attention_ms_mean": t["attn_ms_mean"], "attention_ms_min": t["attn_ms_min"],
            "attention_tflops": attn, "attention_frac_bf16_peak": attn / PEAK_BF16_TFLOPS,
+           "attention_mfma_work_frac": attn * padded_work_factor(w.head_dim) / PEAK_BF16_TFLOPS,
            "qknorm_rope_ms": t["norm_ms"], "qknorm_rope_frac_hbm": norm_bytes / (t["norm_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
            "token_metadata_ms": t["meta_ms"],
            "kernel": kernel_label(w.head_dim, False, step.fused)}
@@ -811,6 +822,7 @@ def main(argv=None) -> int:
                    "q_norm": "inside the attention kernel" if step.fused else "norm kernel (Q' through HBM)"},
         "pct_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
         "attention_only": {"tflops": attn_tflops, "pct_bf16_peak": 100.0 * attn_tflops / PEAK_BF16_TFLOPS,
+                           "mfma_work_frac": attn_tflops * padded_work_factor(w.head_dim) / PEAK_BF16_TFLOPS,
                            "ms_mean": t["attn_ms_mean"], "ms_median": t["attn_ms_median"],
                            "ms_min": t["attn_ms_min"]},
         "qknorm_rope": {"heads": "k only" if step.fused else "q and k", "ms": t["norm_ms"], "gbs": norm_bytes / (t["norm_ms"] * 1e-3) / 1e9,

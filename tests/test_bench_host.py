@@ -169,3 +169,10 @@ def test_kernel_label_names_the_launched_instance(head_dim, padded, fused, want)
     """The label in the line names the template instance the launcher picks
     for the head dim (65..80 runs as the 80-channel instance)."""
     assert bench.kernel_label(head_dim, padded, fused) == want
+
+
+@pytest.mark.parametrize("head_dim,want", [(128, 1.0), (64, 1.0), (72, (80 + 96) / 144.0), (96, 1.0), (40, 128 / 80.0)])
+def test_padded_work_factor(head_dim, want):
+    """MFMA work per useful FLOP from head-dim padding: QK^T over the kernel
+    instance's channels, PV in 32-channel blocks."""
+    assert bench.padded_work_factor(head_dim) == pytest.approx(want)
