@@ -349,6 +349,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   const uint32_t vo_kc = (uint32_t)(lr * rkc) + lcol + loob, vo_vc = (uint32_t)(lr * rvc) + lcol + loob;
   const uint32_t vo_kn = (uint32_t)(lr * rkn) + lcol + loob, vo_vn = (uint32_t)(lr * rvn) + lcol + loob;
   constexpr int kSlab = 4 * NW;  // rows per load instruction and work-group
+  // Byte offsets are formed in unsigned 32-bit arithmetic: a row just past the
+  // end of a slice whose span is close to 2^31 bytes has an offset above 2^31,
+  // which reads as zeros (past the extent) and must not be a signed overflow.
   // A tile past the work-group's last one is still issued, through a resource
   // of extent zero (every lane reads zeros, nothing is fetched), so that each
   // issue is exactly LOADS unmasked instructions per wave and the waits below
@@ -374,7 +377,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
       const uint32_t o = pick(cached, pick(is_k, vo_kc, vo_vc), pick(is_k, vo_kn, vo_vn));
       const int r0 = cached ? k0 : k0 - P;
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i) dma16(r, d0 + 1024 * NW * i, (int)(o + (uint32_t)((r0 + kSlab * i) * st)));
+      for (int i = 0; i < LOADS; ++i) dma16(r, d0 + 1024 * NW * i, (int)(o + (uint32_t)(r0 + kSlab * i) * (uint32_t)st));
     } else {
       const __amdgpu_buffer_rsrc_t rc = pick(is_k, rs_kc, rs_vc);
       const __amdgpu_buffer_rsrc_t rn = pick(is_k, rs_kn, rs_vn);
@@ -383,8 +386,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
         const int key = k0 + kSlab * i + lr;
-        if (key < P) dma16(rc, d0 + 1024 * NW * i, (int)(oc + (uint32_t)((k0 + kSlab * i) * sc)));
-        if (key >= P) dma16(rn, d0 + 1024 * NW * i, (int)(on + (uint32_t)((k0 - P + kSlab * i) * sn)));
+        if (key < P) dma16(rc, d0 + 1024 * NW * i, (int)(oc + (uint32_t)(k0 + kSlab * i) * (uint32_t)sc));
+        if (key >= P) dma16(rn, d0 + 1024 * NW * i, (int)(on + (uint32_t)(k0 - P + kSlab * i) * (uint32_t)sn));
       }
     }
   };

@@ -322,6 +322,31 @@ void attention_cases() {
   expect("cached pointers", g_attn.kc == FAKE3 && g_attn.vc == FAKE3 + 0x1000 && g_attn.P == 16 &&
                                 g_attn.Snew == 100 && g_attn.Sk == 116 && g_attn.scale == 0.25f);
 
+  // Keys are addressed with 32-bit byte offsets inside one (batch, kv-head)
+  // slice: 4000 keys 536864 bytes apart (2,147,456,000 bytes) are accepted,
+  // 536880 bytes apart (2,147,520,000) refused -- for new keys and for a cache.
+  {
+    const int64_t qs[3] = {4000LL * 4 * 128, 4 * 128, 128}, qn[3] = {130LL * 4 * 128, 4 * 128, 128};
+    const int64_t ks[3] = {4000LL * 268432, 268432, 128}, kb[3] = {4000LL * 268440, 268440, 128};
+    const int64_t ok4[4][3] = {{qs[0], qs[1], qs[2]}, {ks[0], ks[1], ks[2]}, {ks[0], ks[1], ks[2]}, {qs[0], qs[1], qs[2]}};
+    const int64_t bad4[4][3] = {{qs[0], qs[1], qs[2]}, {kb[0], kb[1], kb[2]}, {ks[0], ks[1], ks[2]}, {qs[0], qs[1], qs[2]}};
+    OK_LAUNCHES(dit_attn_forward(FAKE, FAKE2, FAKE3, FAKE, nullptr, 1, 4000, 4, 1, 128, ok4, 0, nullptr, 0.f, 0, nullptr),
+                1);
+    ERR(dit_attn_forward(FAKE, FAKE2, FAKE3, FAKE, nullptr, 1, 4000, 4, 1, 128, bad4, 0, nullptr, 0.f, 0, nullptr),
+        DIT_ATTN_ERR_UNSUPPORTED);
+    const int64_t ok6[6][3] = {{qn[0], qn[1], qn[2]}, {ks[0], ks[1], ks[2]}, {ks[0], ks[1], ks[2]},
+                               {qn[0], qn[1], qn[2]}, {qn[0], qn[1], qn[2]}, {qn[0], qn[1], qn[2]}};
+    const int64_t bad6[6][3] = {{qn[0], qn[1], qn[2]}, {ks[0], ks[1], ks[2]}, {kb[0], kb[1], kb[2]},
+                                {qn[0], qn[1], qn[2]}, {qn[0], qn[1], qn[2]}, {qn[0], qn[1], qn[2]}};
+    OK_LAUNCHES(dit_attn_forward_cached(FAKE, FAKE2, FAKE3, FAKE, FAKE + 0x1000, FAKE2 + 0x1000, nullptr, 1, 4000, 130,
+                                        4, 1, 128, ok6, 0, nullptr, 0.f, 0, nullptr),
+                1);
+    expect("span limit cache", g_attn.P == 4000 && g_attn.Snew == 130 && g_attn.Sk == 4130);
+    ERR(dit_attn_forward_cached(FAKE, FAKE2, FAKE3, FAKE, FAKE + 0x1000, FAKE2 + 0x1000, nullptr, 1, 4000, 130, 4, 1,
+                                128, bad6, 0, nullptr, 0.f, 0, nullptr),
+        DIT_ATTN_ERR_UNSUPPORTED);
+  }
+
   // Padded forms.
   const uint64_t* kb = reinterpret_cast<const uint64_t*>(FAKE2 + 0x100000);
   auto fp = [&](const void* q, const uint64_t* bits, int64_t words, int32_t S, int32_t B,
