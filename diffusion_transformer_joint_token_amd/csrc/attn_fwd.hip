@@ -805,37 +805,49 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
 
 // fp32 path: one thread per query row, K/V tiles of 32 keys in LDS, exact
 // online softmax per tile.  Used for fp32 inputs (parity-grade small shapes).
+// fp32 path: one work-group of 256 threads per 64 query rows of one
+// (batch, head); each row is split over 4 neighbouring lanes that hold DP/4
+// channels of q and O each (so no head dim needs private memory), and a score
+// is the sum of the 4 partial dot products (two exchanges within the group).
+// Keys go through LDS in tiles of 32 with an exact online softmax per tile.
 template <int DP>
-__global__ __launch_bounds__(64) void attn_fwd_f32_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256) void attn_fwd_f32_kernel(AttnArgs a) {
   constexpr int TK = 32;
+  constexpr int CH = DP / 4;  // channels per lane
   __shared__ float sk[TK][DP];
   __shared__ float sv[TK][DP];
+  __shared__ int s_lim[4];
   const int tid = threadIdx.x;
+  const int c = tid & 3;  // lane within the row's group: channels c*CH .. c*CH + CH-1
   const int n_qtiles = (a.Snew + 63) / 64;
   const int bh = blockIdx.x / n_qtiles;
   const int qt = blockIdx.x % n_qtiles;
   const int h = bh % a.H;
   const int b = bh / a.H;
   const int kvh = h / (a.H / a.Hk);
-  const int qrow = qt * 64 + tid;
+  const int qrow = qt * 64 + (tid >> 2);
   const bool row_ok = qrow < a.Snew;
   const int qclamp = row_ok ? qrow : a.Snew - 1;
   const int lim = a.kv_limit ? a.kv_limit[a.P + qclamp] : a.Sk;
   const uint64_t* kbits = a.key_bits ? a.key_bits + (int64_t)b * a.kb_stride : nullptr;
   int wlim = lim;
   for (int m = 32; m >= 1; m >>= 1) wlim = max(wlim, __shfl_xor(wlim, m, 64));
+  if ((tid & 63) == 0) s_lim[tid >> 6] = wlim;
+  __syncthreads();
+  wlim = max(max(s_lim[0], s_lim[1]), max(s_lim[2], s_lim[3]));
 
-  float q[DP], o[DP];
+  float q[CH], o[CH];
   const float* qp = reinterpret_cast<const float*>(a.q) + b * a.qs[0] + (int64_t)qclamp * a.qs[1] + h * a.qs[2];
 #pragma unroll
-  for (int d = 0; d < DP; ++d) {
-    q[d] = d < a.D ? qp[d] : 0.f;
+  for (int d = 0; d < CH; ++d) {
+    const int dd = c * CH + d;
+    q[d] = dd < a.D ? qp[dd] : 0.f;
     o[d] = 0.f;
   }
   float m_cur = -INFINITY, l = 0.f;
   for (int k0 = 0; k0 < wlim; k0 += TK) {
     __syncthreads();
-    for (int e = tid; e < TK * DP; e += 64) {
+    for (int e = tid; e < TK * DP; e += 256) {
       const int r = e / DP, d = e % DP;
       int key = k0 + r;
       key = key < a.Sk ? key : a.Sk - 1;
@@ -862,7 +874,9 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(AttnArgs a) {
     for (int j = 0; j < TK; ++j) {
       float acc = 0.f;
 #pragma unroll
-      for (int d = 0; d < DP; ++d) acc = fmaf(q[d], sk[j][d], acc);
+      for (int d = 0; d < CH; ++d) acc = fmaf(q[d], sk[j][c * CH + d], acc);
+      acc += __shfl_xor(acc, 1, 64);
+      acc += __shfl_xor(acc, 2, 64);
       s[j] = (k0 + j < lim && ((vbits >> j) & 1u)) ? acc * a.scale : -INFINITY;
       mx = fmaxf(mx, s[j]);
     }
@@ -871,13 +885,13 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(AttnArgs a) {
       const float alpha = expf(m_cur - m_new);
       l *= alpha;
 #pragma unroll
-      for (int d = 0; d < DP; ++d) o[d] *= alpha;
+      for (int d = 0; d < CH; ++d) o[d] *= alpha;
 #pragma unroll
       for (int j = 0; j < TK; ++j) {
         const float p = expf(s[j] - m_new);
         l += p;
 #pragma unroll
-        for (int d = 0; d < DP; ++d) o[d] = fmaf(p, sv[j][d], o[d]);
+        for (int d = 0; d < CH; ++d) o[d] = fmaf(p, sv[j][c * CH + d], o[d]);
       }
       m_cur = m_new;
     }
@@ -886,8 +900,11 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(AttnArgs a) {
     float* op = reinterpret_cast<float*>(a.o) + b * a.os[0] + (int64_t)qrow * a.os[1] + h * a.os[2];
     // A row with no valid key (padding) has l = 0: O = 0, lse = -inf.
     const float inv = l > 0.f ? 1.0f / l : 0.f;
-    for (int d = 0; d < a.D; ++d) op[d] = o[d] * inv;
-    if (a.lse != nullptr) a.lse[((int64_t)b * a.H + h) * a.Snew + qrow] = l > 0.f ? m_cur + logf(l) : -INFINITY;
+#pragma unroll
+    for (int d = 0; d < CH; ++d)
+      if (c * CH + d < a.D) op[c * CH + d] = o[d] * inv;
+    if (a.lse != nullptr && c == 0)
+      a.lse[((int64_t)b * a.H + h) * a.Snew + qrow] = l > 0.f ? m_cur + logf(l) : -INFINITY;
   }
 }
 
@@ -936,7 +953,7 @@ template <int DP>
 hipError_t launch_f32(const AttnArgs& a, hipStream_t stream) {
   const int n_qtiles = (a.Snew + 63) / 64;
   const long long nblocks = (long long)n_qtiles * a.B * a.H;
-  hipLaunchKernelGGL((attn_fwd_f32_kernel<DP>), dim3((unsigned)nblocks), dim3(64), 0, stream, a);
+  hipLaunchKernelGGL((attn_fwd_f32_kernel<DP>), dim3((unsigned)nblocks), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
