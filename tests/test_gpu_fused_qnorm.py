@@ -83,6 +83,8 @@ FUSED_CASES = [
     (2, 2, 2, 32, (("T", 70), ("I", 1, 6, 6)), (8, 12, 12), "block_causal", 64, False, "random"),
     (1, 1, 1, 128, (("T", 1),), (16, 56, 56), "block_causal", 0, False, None),
     (1, 2, 1, 8, (("I", 1, 4, 6),), (4, 2, 2), "full", 0, False, None),
+    # head dim 72 on the 80-channel instance with a 64-aligned cached prefix and padded text (GQA 4:1)
+    (2, 4, 1, 72, (("T", 64), ("I", 1, 8, 12), ("T", 20)), (24, 24, 24), "block_causal", 64, False, "right"),
     # time-aware rotary scaling (the Lumina-Next factors) with the per-head RMSNorm
     (2, 4, 2, 72, (("I", 1, 12, 18),), (24, 24, 24), "full", 0, False, None, 2.0, 1.0),
     (1, 4, 4, 128, (("T", 70), ("I", 1, 8, 12)), (16, 56, 56), "block_causal", 64, False, None, 1.0, 3.0),
