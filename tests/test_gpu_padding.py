@@ -405,3 +405,34 @@ def test_image_query_workload_sampled(dit):
     _check_lse(lse[:, :, idx].cpu().double().numpy(), rl, w.dtype)
     _say("  valid text %s rows=%d max=%.3g mean=%.3g" % (tv.sum(axis=1).tolist(), rows.size, stats["max"],
                                                         stats["mean"]))
+
+
+def test_metadata_and_key_valid_at_maximum_sizes(dit):
+    """A ~250k-token joint sequence (multi-frame blocks, hundreds of 1024-token
+    chunks, the checker's scan over the whole mask) and exactly MAX_IMAGES
+    (64) image blocks: token metadata and key-validity bits bit-exact against
+    the oracle.  One block more is refused on the host."""
+    from diffusion_transformer_joint_token_amd import _lib
+    big = (("T", 3000), ("I", 4, 160, 160), ("T", 777), ("I", 1, 256, 256), ("T", 5), ("I", 2, 200, 200))
+    many = tuple(seg for _ in range(_lib.MAX_IMAGES) for seg in (("T", 3), ("I", 1, 2, 2)))
+    for layout, tag in ((big, "250k tokens"), (many, "64 image blocks")):
+        w = wl.small_workload("max", 2, 1, 1, 8, layout, (8,))
+        mask, shapes = wl.sequence_inputs(w)
+        _say("maximum sizes: %s (S=%d, %d blocks)" % (tag, w.seq_len, len(shapes)))
+        ref = ometa.build_token_metadata(mask, shapes, "centered_fhw")
+        m = dit.build_token_metadata(torch.from_numpy(mask).cuda(), shapes, "centered_fhw")
+        m.check()
+        for key in ("image_ids", "target_mask", "pos_ids", "kv_limit"):
+            got = getattr(m, key).cpu().numpy()
+            assert np.array_equal(got, ref[key].astype(got.dtype)), (tag, key)
+        tv = wl.text_mask(w, 21, "random")
+        kv = _build(dit, mask, tv)
+        torch.cuda.synchronize()
+        assert np.array_equal(_gpu_bits(kv), pack_bits(okp.joint_key_valid(mask, tv))), tag
+    over = many + (("T", 3), ("I", 1, 2, 2))
+    w = wl.small_workload("over", 1, 1, 1, 8, over, (8,))
+    mask, shapes = wl.sequence_inputs(w)
+    assert len(shapes) == _lib.MAX_IMAGES + 1
+    with pytest.raises(dit.DitAttnError) as err:
+        dit.build_token_metadata(torch.from_numpy(mask).cuda(), shapes, "centered_fhw")
+    assert err.value.status == _lib.ERR_SHAPE
